@@ -1,0 +1,155 @@
+"""Seeded synthetic inputs for the spatial/temporal sparse attention path.
+
+This module only draws random numbers and arranges them into tensors of the
+video-DiT shapes below; it holds none of the method's arithmetic (no masks,
+no softmax, no norm, no rotary embedding, no profiling).  Both the CPU oracle
+side and the GPU side of the tests, and the benchmark, take their inputs from
+here, so the two sides always see identical bf16 values.
+
+Shapes follow the token grids of the models the Sparse VideoGen pages name
+(CogVideoX, Wan 2.1, HunyuanVideo at 720p).  No model weights, prompts or
+videos exist here: Q/K/V are random activations with a planted per-head
+structure so that some heads prefer the spatial mask and others the temporal
+mask:
+
+* a "spatial-planted" head adds one shared random vector per (head, frame) to
+  every Q and K row of that frame, so queries correlate with keys of their own
+  frame;
+* a "temporal-planted" head adds one shared random vector per (head, in-frame
+  position) to every Q and K row at that position, so queries correlate with
+  keys at the same location in every frame.
+
+V is unstructured N(0, 1).
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, Optional
+
+import numpy as np
+import torch
+
+SPATIAL = 0
+TEMPORAL = 1
+DENSE = 2
+
+
+@dataclasses.dataclass(frozen=True)
+class Geometry:
+    """Batch B, heads H, a token grid of F frames x HH rows x WW columns, head dim D."""
+    B: int
+    H: int
+    F: int
+    HH: int
+    WW: int
+    D: int
+
+    @property
+    def P(self) -> int:
+        return self.HH * self.WW
+
+    @property
+    def S(self) -> int:
+        return self.F * self.HH * self.WW
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    geom: Geometry
+    w_f: int              # spatial window: frames either side
+    w_p: int              # temporal band: in-frame positions either side
+    n_q: int              # profiled query count
+    seed: int             # Q/K/V seed
+    idx_seed: int         # query-sample seed
+    planted: bool         # plant spatial/temporal structure
+    plant_scale: float = 2.0
+    norm_rope: bool = False
+    rope_base: float = 10000.0
+    eps: float = 1e-6
+
+
+# The five workloads: the tiny case the oracle finishes in seconds, three
+# model-shaped token grids, and the full per-layer step at the 720p grid.
+WORKLOADS: Dict[str, Workload] = {
+    "tiny": Workload("tiny", Geometry(1, 2, 4, 8, 8, 64), 1, 2, 64, 1, 101, planted=False),
+    "cogvideox": Workload("cogvideox", Geometry(1, 48, 13, 30, 45, 64), 1, 8, 64, 2, 102, planted=True),
+    "wan": Workload("wan", Geometry(1, 40, 21, 30, 52, 128), 1, 8, 64, 3, 103, planted=True, norm_rope=True),
+    "hunyuan720p": Workload("hunyuan720p", Geometry(1, 24, 33, 45, 80, 128), 1, 64, 64, 4, 104, planted=True),
+    "hunyuan720p_step": Workload("hunyuan720p_step", Geometry(1, 24, 33, 45, 80, 128), 1, 64, 64, 50, 150,
+                                 planted=True, norm_rope=True),
+    # the 4-frame sub-grid of the 720p step, small enough for the oracle in full
+    "hunyuan720p_f4": Workload("hunyuan720p_f4", Geometry(1, 24, 4, 45, 80, 128), 1, 64, 64, 60, 160,
+                               planted=True, norm_rope=True),
+}
+
+
+def planted_kinds(H: int, seed: int) -> np.ndarray:
+    """Seeded half/half assignment of heads to planted kinds (uint8 [H])."""
+    rng = np.random.default_rng(seed + 7919)
+    order = rng.permutation(H)
+    kinds = np.full(H, TEMPORAL, dtype=np.uint8)
+    kinds[order[: H // 2]] = SPATIAL
+    return kinds
+
+
+def sample_queries(S: int, n_q: int, seed: int) -> np.ndarray:
+    """Uniform sample of n_q distinct query rows of [0, S), int32, one set per call."""
+    rng = np.random.default_rng(seed)
+    return np.sort(rng.choice(S, size=n_q, replace=False)).astype(np.int32)
+
+
+def norm_weights(D: int, seed: int):
+    """Two learned-weight stand-ins ~ U(0.5, 1.5), fp32 [D] each (for Q and for K)."""
+    rng = np.random.default_rng(seed + 31)
+    wq = rng.uniform(0.5, 1.5, size=D).astype(np.float32)
+    wk = rng.uniform(0.5, 1.5, size=D).astype(np.float32)
+    return wq, wk
+
+
+def _plant(x: torch.Tensor, geom: Geometry, kinds: np.ndarray, u_sp: torch.Tensor, u_tp: torch.Tensor,
+           scale: float) -> None:
+    """In place: x[b, h] += scale * shared vector of the row's group (frame or position)."""
+    B, H, F, P, D = geom.B, geom.H, geom.F, geom.P, geom.D
+    xv = x.view(B, H, F, P, D)
+    for h in range(H):
+        if kinds[h] == SPATIAL:
+            xv[:, h] += scale * u_sp[h].view(1, F, 1, D)
+        else:
+            xv[:, h] += scale * u_tp[h].view(1, 1, P, D)
+
+
+def make_qkv(wl: Workload, device: str = "cpu", layer: int = 0, dtype=torch.bfloat16):
+    """Q, K, V as [B, H, S, D] tensors of `dtype` (bf16 by default; RNE from fp32).
+
+    Values are drawn in fp32 with a seeded generator on `device` and cast once.
+    On "cpu" the draw is bit-reproducible everywhere; on a GPU it is
+    reproducible for a given device type.  `layer` offsets the seed so that
+    each layer of a multi-layer step gets fresh activations.
+    """
+    g = wl.geom
+    gen = torch.Generator(device=device)
+    gen.manual_seed(wl.seed * 1000 + layer)
+    shape = (g.B, g.H, g.S, g.D)
+    q = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    k = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    v = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    if wl.planted:
+        kinds = planted_kinds(g.H, wl.seed * 1000 + layer)
+        u_sp = torch.randn((g.H, g.F, g.D), generator=gen, device=device, dtype=torch.float32)
+        u_tp = torch.randn((g.H, g.P, g.D), generator=gen, device=device, dtype=torch.float32)
+        _plant(q, g, kinds, u_sp, u_tp, wl.plant_scale)
+        _plant(k, g, kinds, u_sp, u_tp, wl.plant_scale)
+        del u_sp, u_tp
+    return q.to(dtype), k.to(dtype), v.to(dtype)
+
+
+def expected_planted_kinds(wl: Workload, layer: int = 0) -> Optional[np.ndarray]:
+    if not wl.planted:
+        return None
+    return planted_kinds(wl.geom.H, wl.seed * 1000 + layer)
+
+
+def bf16_to_f64(t: torch.Tensor) -> np.ndarray:
+    """Exact widening of a bf16 (or fp32) tensor to a float64 numpy array."""
+    return t.detach().to("cpu").to(torch.float64).numpy()
