@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse 3D attention path at the HunyuanVideo-720p token grid on one MI355X.
+
+A step is one layer of the path over one batch of synthetic activations already resident in
+HBM: QK-RMSNorm + 3D RoPE -> per-head profiling on 64 sampled queries -> token-major copies
+of the temporal heads' Q/K/V -> block-sparse attention -> frame-major output.  Steps cycle
+over 4 layers of fresh seeded inputs (B=1, H=24, F=33 x 45 x 80 tokens = 118800, D=128,
+bf16, half the heads planted spatial and half temporal; w_f = 1 frame, w_p = 64 positions).
+
+Prints one JSON line on stdout (progress goes to stderr).  `value` is the effective
+attention throughput of the whole step: FLOPs of the computed attention tiles (4*D per
+query-key pair of every 128x64 tile the schedule computes, clipped at the sequence end)
+divided by the step time.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_hunyuan720p_traffic.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=12)
+    ap.add_argument("--warmup", type=int, default=4)
+    ap.add_argument("--layers", type=int, default=4)
+    return ap.parse_args()
+
+
+def tile_flops(svg, kind, g, w_f, w_p, bm, bn):
+    """FLOPs of the tiles the schedule computes (from the library's exported block mask)."""
+    import torch
+    mask = svg.build_block_mask(kind, g.F, g.HH, g.WW, w_f, w_p, bm, bn).to(torch.float64)
+    S = g.S
+    rows = torch.full((mask.shape[2],), float(bm), dtype=torch.float64, device=mask.device)
+    rows[-1] = S - bm * (mask.shape[2] - 1)
+    cols = torch.full((mask.shape[3],), float(bn), dtype=torch.float64, device=mask.device)
+    cols[-1] = S - bn * (mask.shape[3] - 1)
+    pairs = torch.einsum("bhij,i,j->", mask, rows, cols).item()
+    return 4.0 * g.D * pairs
+
+
+def token_flops(kind_np, g, w_f, w_p):
+    """4*D per allowed (query, key) pair: the token-level work of the masks."""
+    def band(n_groups, group, w):
+        return group * group * sum(min(n_groups - 1, i + w) - max(0, i - w) + 1 for i in range(n_groups))
+    per = {0: band(g.F, g.P, w_f), 1: band(g.P, g.F, w_p), 2: g.S * g.S}
+    return 4.0 * g.D * sum(per[int(k)] for k in kind_np.ravel())
+
+
+def kernel_sha():
+    h = hashlib.sha256()
+    for f in ("attn_fwd.hip", "svg_internal.h"):
+        with open(os.path.join(ROOT, "spatial_temporal_sparse_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the attention kernel from the committed counter runs, if they
+    were taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sha") != kernel_sha():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(q, k, v, kinds, g, w_f, w_p):
+    """The fp64 oracle on a bounded sample of the same layer: 512 query rows of one spatial
+    and one temporal head against all 118800 keys; token-level FLOPs / wall time."""
+    import numpy as np
+    import oracle.svg_oracle as O
+    try:
+        import threadpoolctl
+        threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
+    except Exception:  # threadpoolctl missing: report the affinity size
+        threads = len(os.sched_getaffinity(0))
+    heads = [int(np.argmax(kinds == 0)), int(np.argmax(kinds == 1))]
+    rng = np.random.default_rng(123)
+    rows = np.sort(rng.choice(g.S, 512, replace=False))
+    sc = 1.0 / math.sqrt(g.D)
+    flops = 0.0
+    elapsed = 0.0
+    for h in heads:
+        f64 = lambda t: t[0, h].detach().cpu().double().numpy()
+        qh, kh, vh = f64(q), f64(k), f64(v)
+        kind = int(kinds[h])
+        t0 = time.perf_counter()
+        O.head_attention_rows(qh, kh, vh, rows, kind, g.F, g.P, w_f, w_p, sc)
+        elapsed += time.perf_counter() - t0
+        m = O.mask_rows(kind, rows, g.S, g.P, w_f, w_p)
+        flops += 4.0 * g.D * float(m.sum())
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": "fp64 numpy oracle, sparse attention of 512 sampled query rows of one spatial and one "
+                      "temporal head of the 720p layer (S=118800, D=128) against all keys; token-level FLOPs",
+            "seconds": round(elapsed, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards over heads with no "
+              f"exchange, so per-GPU throughput is the one-GPU figure.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import spatial_temporal_sparse_amd as svg
+    from workloads import WORKLOADS, make_qkv, norm_weights, sample_queries
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = WORKLOADS["hunyuan720p_step"]
+    g = wl.geom
+    L = max(1, args.layers)
+    log(f"[bench] generating {L} layers of {g} on {torch.cuda.get_device_name(dev)}")
+    layers = []
+    for l in range(L):
+        q, k, v = make_qkv(wl, device="cuda", layer=l)
+        idx = torch.from_numpy(sample_queries(g.S, wl.n_q, wl.idx_seed + l)).to(dev)
+        layers.append((q, k, v, idx))
+    wq, wk = norm_weights(g.D, wl.seed)
+    norm = (torch.from_numpy(wq).to(dev), torch.from_numpy(wk).to(dev), wl.eps, wl.rope_base)
+    bufs = svg.LayerBuffers(layers[0][0], wl.n_q, g.F, g.HH, g.WW)
+    bm, bn = svg.tile_shape()
+    F, HH, WW, w_f, w_p = g.F, g.HH, g.WW, wl.w_f, wl.w_p
+
+    def step(l, ev=None):
+        q, k, v, idx = layers[l]
+        if ev is not None:
+            ev[0].record()
+        qn, kn = svg.qknorm_rope(q, k, norm[0], norm[1], F, HH, WW, wl.eps, wl.rope_base, q_out=bufs.qn, k_out=bufs.kn)
+        if ev is not None:
+            ev[1].record()
+        svg.profile_heads(qn, kn, v, idx, F, HH, WW, w_f, w_p, mse=bufs.mse, kind=bufs.kind, ws=bufs.ws_profile)
+        if ev is not None:
+            ev[2].record()
+        svg.permute(qn, F, HH, WW, bufs.kind, svg.TEMPORAL, out=bufs.qt)
+        svg.permute(kn, F, HH, WW, bufs.kind, svg.TEMPORAL, out=bufs.kt)
+        svg.permute(v, F, HH, WW, bufs.kind, svg.TEMPORAL, out=bufs.vt)
+        if ev is not None:
+            ev[3].record()
+        svg.sparse_attn(qn, kn, v, bufs.qt, bufs.kt, bufs.vt, bufs.kind, F, HH, WW, w_f, w_p, o=bufs.o, ot=bufs.ot,
+                        ws=bufs.ws_attn)
+        if ev is not None:
+            ev[4].record()
+        svg.unpermute(bufs.ot, F, HH, WW, bufs.kind, svg.TEMPORAL, out=bufs.o)
+        if ev is not None:
+            ev[5].record()
+
+    # one untimed pass per layer: the kinds each layer chooses fix its tile work
+    kinds, flops_tile, flops_tok = [], [], []
+    for l in range(L):
+        step(l)
+        kd = bufs.kind.clone()
+        kinds.append(kd.cpu().numpy()[0])
+        flops_tile.append(tile_flops(svg, kd, g, w_f, w_p, bm, bn))
+        flops_tok.append(token_flops(kd.cpu().numpy(), g, w_f, w_p))
+    torch.cuda.synchronize()
+    log(f"[bench] kinds per layer: {[k.tolist() for k in kinds]}")
+
+    for i in range(args.warmup):
+        step(i % L)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps")
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i % L, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    stage = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(5)] for i in range(args.steps)])
+    names = ["qknorm_rope", "profile_heads", "permute_qkv", "sparse_attn", "unpermute"]
+    stage_ms = {n: float(stage[:, j].mean()) for j, n in enumerate(names)}
+    step_tile = np.array([flops_tile[i % L] for i in range(args.steps)])
+    step_tok = np.array([flops_tok[i % L] for i in range(args.steps)])
+    attn_ms = stage[:, 3]
+    attn_tflops = float(np.mean(step_tile / (attn_ms * 1e-3)) / 1e12)
+    log(f"[bench] {ms_per_step:.3f} ms/step; stages {json.dumps({k: round(v, 4) for k, v in stage_ms.items()})}")
+
+    # HBM-bound stages: algorithmic bytes over time
+    BH, S, D = g.B * g.H, g.S, g.D
+    n_tmp = np.array([int((kinds[i % L] == 1).sum()) for i in range(args.steps)])
+    row = S * D * 2
+    hbm = {
+        "qknorm_rope": float(np.mean(4 * BH * row / (stage[:, 0] * 1e-3)) / 1e9),
+        "permute_qkv": float(np.mean(6 * n_tmp * row / (stage[:, 2] * 1e-3)) / 1e9),
+        "unpermute": float(np.mean(2 * n_tmp * row / (stage[:, 4] * 1e-3)) / 1e9),
+        "profile_heads": float(np.mean(2 * BH * row / (stage[:, 1] * 1e-3)) / 1e9),
+    }
+
+    # the same kernel run dense, on layer 0
+    q, k, v, _ = layers[0]
+    svg.dense_attn(q, k, v, F, HH, WW, o=bufs.o)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    svg.dense_attn(q, k, v, F, HH, WW, o=bufs.o)
+    e1.record()
+    torch.cuda.synchronize()
+    dense_ms = e0.elapsed_time(e1)
+    dense_flops = 4.0 * S * S * D * BH
+
+    traffic = measured_traffic()
+    tile_per_launch = float(step_tile.mean())
+    result = {
+        "metric": "sparse-attn ms/layer + effective TFLOP/s (% bf16 MFMA peak), 720p shape",
+        "value": round(float(np.mean(step_tile)) / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "hunyuan720p_step: one layer (qknorm+rope, profile 64 queries, permute, "
+                               "block-sparse attention, unpermute) over 4 layers of fresh inputs",
+                   "B": g.B, "H": g.H, "F": g.F, "HH": g.HH, "WW": g.WW, "S": S, "D": D, "w_f": w_f, "w_p": w_p,
+                   "n_q": wl.n_q, "layers": L, "tile": [bm, bn], "parallelism": "single GPU"},
+        "sparse_attn_ms": round(float(attn_ms.mean()), 4),
+        "sparse_attn_tflops": round(attn_tflops, 2),
+        "sparse_attn_frac_of_bf16_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+        "tile_tflop_per_layer": round(tile_per_launch / 1e12, 4),
+        "token_tflop_per_layer": round(float(step_tok.mean()) / 1e12, 4),
+        "dense_attn_ms": round(dense_ms, 3),
+        "dense_attn_tflops": round(dense_flops / (dense_ms * 1e-3) / 1e12, 2),
+        "speedup_vs_dense_kernel": round(dense_ms / float(attn_ms.mean()), 3),
+        "speedup_vs_dense_step": round((stage_ms["qknorm_rope"] + dense_ms) / ms_per_step, 3),
+        "profile_over_attn": round(stage_ms["profile_heads"] / stage_ms["sparse_attn"], 4),
+        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "hbm_gbs": {k: round(v, 1) for k, v in hbm.items()},
+        "hbm_frac_of_peak": {k: round(v / PEAK_HBM_GBS, 3) for k, v in hbm.items()},
+        "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel<128>", "achieved": round(attn_tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+    }
+    log("[bench] timing the CPU oracle on a bounded sample")
+    qn = bufs.qn  # the last layer's normalised Q/K; pair them with that layer's V
+    last = (args.steps - 1) % L
+    result["cpu_baseline"] = cpu_baseline(qn, bufs.kn, layers[last][2], kinds[last], g, w_f, w_p)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

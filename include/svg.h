@@ -1,0 +1,183 @@
+/*
+ * svg.h -- C ABI of libsvg: the per-layer hot path of Sparse VideoGen's
+ * spatial/temporal sparse 3D attention on one MI355X (gfx950).
+ *
+ * Sources cited below:
+ *   [svg-authors] "Sparse VideoGen: Accelerating Video Diffusion Transformers with
+ *                 Spatial-Temporal Sparsity", the authors' article (dtcms.com repost,
+ *                 wzjs/233309).
+ *   [svg-jqzx]    机器之心's ICML 2025 article on Sparse VideoGen (xinfinite.net repost,
+ *                 t/topic/12021).
+ *   [svg2-gist]   "Sparse VideoGen2: Accelerate Video Generation with Sparse Attention
+ *                 via Semantic-Aware Permutation", explainer at gist.science (2505.18875).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Geometry.  A latent video is F frames of an HH x WW token grid: P = HH*WW tokens per
+ *   frame and S = F*P tokens.  Frame-major order (the model's) indexes token (f, y, x) as
+ *   t = f*P + y*WW + x.  Token-major order indexes it as u = p*F + f with p = y*WW + x.
+ * Tensors.  Q, K, V and outputs are [B][H][S][D] arrays, row-major, D contiguous, bf16
+ *   (2-byte bfloat16) unless a call says otherwise.  D must be 64 or 128.
+ * Memory.  Every tensor pointer is a DEVICE pointer owned by the caller and must be
+ *   16-byte aligned.  The library allocates no device memory; calls that need scratch
+ *   memory take a caller-owned workspace `ws` of at least svg_workspace_bytes(...) bytes.
+ * Streams.  `stream` is a hipStream_t (NULL = the null stream).  Every call only enqueues
+ *   work on it and returns; none synchronises the host.  Head kinds and errors written by
+ *   svg_profile_heads stay on the device and are read there by later calls.
+ * Errors.  Calls return svg_status: 0 on success, a negative code on failure.  Arguments
+ *   are checked on the host before anything is enqueued; a failed check enqueues nothing.
+ *   svg_last_error() gives a message for the calling thread's most recent failure.
+ * Kinds.  One uint8 per (b, h) in [B*H] device arrays: SVG_SPATIAL, SVG_TEMPORAL or
+ *   SVG_DENSE.  Kernels treat any other value as SVG_DENSE (a superset of both masks).
+ * Thread safety.  The library keeps no state between calls except the per-thread error
+ *   message; calls on different streams may run concurrently.
+ */
+#ifndef SVG_H
+#define SVG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t svg_status;
+#define SVG_OK               0
+#define SVG_ERR_INVALID     (-1)   /* a null pointer, bad size, bad window, misaligned pointer ... */
+#define SVG_ERR_UNSUPPORTED (-2)   /* a valid request this build does not implement (e.g. D not in {64,128}) */
+#define SVG_ERR_HIP         (-3)   /* the HIP runtime reported an error while enqueueing */
+#define SVG_ERR_WORKSPACE   (-4)   /* ws is NULL or smaller than svg_workspace_bytes() */
+
+/* Head kinds ([svg-authors] Spatial Head / Temporal Head). */
+#define SVG_SPATIAL  0
+#define SVG_TEMPORAL 1
+#define SVG_DENSE    2
+
+/* Workspace-size queries. */
+#define SVG_OP_PROFILE     1
+#define SVG_OP_SPARSE_ATTN 2
+
+typedef struct {
+    int32_t B, H;       /* batch, heads */
+    int32_t F, HH, WW;  /* frames, token-grid rows, token-grid columns: S = F*HH*WW */
+    int32_t D;          /* head dim, 64 or 128 */
+} svg_geom;
+
+typedef struct {
+    int32_t frames;     /* w_f >= 0: a spatial head attends frames f-w_f .. f+w_f (clipped) */
+    int32_t positions;  /* w_p >= 0: a temporal head attends in-frame positions p-w_p .. p+w_p
+                           (flattened p = y*WW + x, clipped) in every frame */
+} svg_windows;
+
+/*
+ * svg_qknorm_rope -- fused QK-RMSNorm and 3D rotary embedding of Q and K.
+ * [svg-authors] closing section and [svg-jqzx] end of the layout section name both
+ * operations as a cost the method optimises; neither page defines them.  Computed here:
+ *   y[c] = x[c] / sqrt(mean_c' x[c']^2 + eps) * w[c]              (over the D channels of a row)
+ *   then channel pairs (2j, 2j+1) of the slice of width n that holds them rotate by
+ *   theta = pos * rope_base^(-2j/n):  (a, b) -> (a cos - b sin, a sin + b cos),
+ *   where the head dim is split into slices [0, dt) | [dt, dt+dh) | [dt+dh, D) whose pos
+ *   is the token's frame f, grid row y and grid column x respectively.
+ * q, k:            bf16 [B][H][S][D] frame-major inputs.
+ * q_out, k_out:    bf16 [B][H][S][D] outputs; may equal q / k (in place).
+ * wq, wk:          fp32 [D] device arrays, shared by all heads.
+ * eps > 0, rope_base > 0; dt, dh, dw >= 0, even, dt + dh + dw == D.
+ * Arithmetic in fp32, round-to-nearest-even on store.  V is not touched.
+ */
+svg_status svg_qknorm_rope(const void* q, const void* k, void* q_out, void* k_out,
+                           const float* wq, const float* wk, float eps, float rope_base,
+                           int32_t dt, int32_t dh, int32_t dw, svg_geom g, void* stream);
+
+/*
+ * svg_profile_heads -- online choice of each head's sparsity pattern.
+ * [svg-jqzx] dynamic adaptive sparsity strategy, steps 1-3, and [svg-authors] Online
+ * Profiling Strategy: for a small random sample of query rows, attention is computed with
+ * the spatial mask, the temporal mask and no mask; each head keeps the mask whose result
+ * is closest to the unmasked one.  Computed here, per (b, h):
+ *   mse_x = mean over the n_q sampled rows and D channels of (O_x - O_dense)^2,  x in {sp, tp}
+ *   kind  = SVG_SPATIAL if mse_sp <= mse_tp (both as stored fp32) else SVG_TEMPORAL.
+ * q, k, v:   bf16 [B][H][S][D] frame-major.
+ * q_idx:     int32 [n_q] device array of frame-major rows in [0, S), one sample for all
+ *            heads; 1 <= n_q <= S.  Out-of-range entries are clamped into [0, S).
+ * w:         the two candidate masks' windows.   scale > 0: softmax scale (1/sqrt(D) usual).
+ * mse_out:   fp32 [B*H][2] device array (spatial, temporal).
+ * kind_out:  uint8 [B*H] device array.
+ * ws:        >= svg_workspace_bytes(SVG_OP_PROFILE, &g, n_q) bytes of device memory.
+ */
+svg_status svg_profile_heads(const void* q, const void* k, const void* v, const int32_t* q_idx, int32_t n_q,
+                             svg_geom g, svg_windows w, float scale, float* mse_out, uint8_t* kind_out,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * svg_permute / svg_unpermute -- the hardware-efficient layout transformation.
+ * [svg-authors] Layout Transformation and [svg-jqzx] layout section: Q, K and V are
+ * reordered along the sequence so that the tokens of one location (all frames) are
+ * adjacent, by transposing the frame x location grid; the output is restored afterwards.
+ *   svg_permute:   dst[b][h][u] = src[b][h][pi(u)],     pi(u)     = (u mod F)*P + u div F
+ *   svg_unpermute: dst[b][h][t] = src[b][h][pi^-1(t)],  pi^-1(t)  = (t mod P)*F + t div P
+ * Rows of D elements of elem_bytes (2 = bf16, 4 = fp32) are copied bit for bit.
+ * Only heads with kind[b*H+h] == select are written; kind == NULL selects every head.
+ * src and dst must not overlap.
+ */
+svg_status svg_permute(const void* src, void* dst, int32_t elem_bytes, const uint8_t* kind, int32_t select,
+                       svg_geom g, void* stream);
+svg_status svg_unpermute(const void* src, void* dst, int32_t elem_bytes, const uint8_t* kind, int32_t select,
+                         svg_geom g, void* stream);
+
+/*
+ * svg_build_block_mask -- which bm x bn tiles of each head's score matrix hold at least one
+ * allowed (query, key) pair, in the head's working layout (token-major for temporal heads,
+ * frame-major otherwise).  This is the schedule svg_sparse_attn follows; it is exported for
+ * inspection.  Patterns: [svg-authors] Spatial Head (blocks around the diagonal) and
+ * Temporal Head (slash lines, contiguous after the layout transformation).
+ * mask_out: uint8 [B*H][ceil(S/bm)][ceil(S/bn)] device array; 1 = tile computed.
+ * bm, bn >= 1 (a tile may exceed the sequence; it is then clipped).
+ */
+svg_status svg_build_block_mask(const uint8_t* kind, svg_geom g, svg_windows w, int32_t bm, int32_t bn,
+                                uint8_t* mask_out, void* stream);
+
+/*
+ * svg_sparse_attn -- block-sparse attention, each head under the mask of its kind.
+ * [svg-authors] Layout Transformation / [svg-jqzx] kernel section: the sparse kernel only
+ * computes the tiles the pattern needs.  Per head, in its working layout:
+ *   O = softmax(scale * Q K^T  restricted to the head's token mask) V
+ * Spatial and dense heads read q, k, v (frame-major) and write o; temporal heads read qt,
+ * kt, vt (token-major, e.g. from svg_permute) and write ot (token-major; restore with
+ * svg_unpermute).  Tiles outside the mask are skipped; inside boundary tiles the exact
+ * token mask is applied.  bf16 inputs, fp32 accumulation, bf16 output.
+ * q, k, v, o, qt, kt, vt, ot: bf16 [B][H][S][D]; the token-major ones may be NULL when no
+ * head is temporal only if kind is NULL.
+ * kind: uint8 [B*H] device array (NULL = every head dense).
+ * ws:   >= svg_workspace_bytes(SVG_OP_SPARSE_ATTN, &g, 0) bytes.
+ */
+svg_status svg_sparse_attn(const void* q, const void* k, const void* v,
+                           const void* qt, const void* kt, const void* vt,
+                           const uint8_t* kind, svg_geom g, svg_windows w, float scale,
+                           void* o, void* ot, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * svg_dense_attn -- unmasked attention with the same kernel: the profiling reference of
+ * [svg-jqzx] step 2 and the attention of the dense early steps in [svg-authors]' other
+ * optimisations.  bf16 [B][H][S][D] in and out, frame-major.
+ */
+svg_status svg_dense_attn(const void* q, const void* k, const void* v, svg_geom g, float scale, void* o,
+                          void* stream);
+
+/* Bytes of workspace a call needs (0 for an invalid request). */
+size_t svg_workspace_bytes(int32_t op, const svg_geom* g, int32_t n_q);
+
+/* Query-block x key-block tile of svg_sparse_attn / svg_dense_attn. */
+void svg_tile_shape(int32_t* bm, int32_t* bn);
+
+/* Static description of a status code. */
+const char* svg_status_string(svg_status s);
+
+/* Message of the calling thread's last failed call ("" if none). */
+const char* svg_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SVG_H */

@@ -1,0 +1,293 @@
+"""Python binding of libsvg: Sparse VideoGen's spatial/temporal sparse 3D attention on MI355X.
+
+Argument marshalling only.  Every step of the path runs in the HIP kernels of libsvg.so;
+PyTorch supplies device memory and the current HIP stream.  Importing this package loads
+the library and raises ImportError if it has not been built
+(``python -m spatial_temporal_sparse_amd.build``); there is no fallback.
+
+Tensors are [B, H, S, D] bf16, contiguous, on one HIP device, with S = F * HH * WW tokens
+in frame-major order (t = f*HH*WW + y*WW + x) unless a function says token-major.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsvg.so")
+
+SPATIAL = 0
+TEMPORAL = 1
+DENSE = 2
+OP_PROFILE = 1
+OP_SPARSE_ATTN = 2
+
+_c_i32 = ctypes.c_int32
+_c_vp = ctypes.c_void_p
+
+
+class Geom(ctypes.Structure):
+    _fields_ = [("B", _c_i32), ("H", _c_i32), ("F", _c_i32), ("HH", _c_i32), ("WW", _c_i32), ("D", _c_i32)]
+
+
+class Windows(ctypes.Structure):
+    _fields_ = [("frames", _c_i32), ("positions", _c_i32)]
+
+
+class SvgError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} [status {status}]")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m spatial_temporal_sparse_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    st = _c_i32
+    sig = {
+        "svg_qknorm_rope": (st, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, ctypes.c_float, ctypes.c_float,
+                                 _c_i32, _c_i32, _c_i32, Geom, _c_vp]),
+        "svg_profile_heads": (st, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, Geom, Windows, ctypes.c_float, _c_vp, _c_vp,
+                                   _c_vp, ctypes.c_size_t, _c_vp]),
+        "svg_permute": (st, [_c_vp, _c_vp, _c_i32, _c_vp, _c_i32, Geom, _c_vp]),
+        "svg_unpermute": (st, [_c_vp, _c_vp, _c_i32, _c_vp, _c_i32, Geom, _c_vp]),
+        "svg_build_block_mask": (st, [_c_vp, Geom, Windows, _c_i32, _c_i32, _c_vp, _c_vp]),
+        "svg_sparse_attn": (st, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, Geom, Windows, ctypes.c_float,
+                                 _c_vp, _c_vp, _c_vp, ctypes.c_size_t, _c_vp]),
+        "svg_dense_attn": (st, [_c_vp, _c_vp, _c_vp, Geom, ctypes.c_float, _c_vp, _c_vp]),
+        "svg_workspace_bytes": (ctypes.c_size_t, [_c_i32, ctypes.POINTER(Geom), _c_i32]),
+        "svg_tile_shape": (None, [ctypes.POINTER(_c_i32), ctypes.POINTER(_c_i32)]),
+        "svg_status_string": (ctypes.c_char_p, [_c_i32]),
+        "svg_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise SvgError(status, f"{lib.svg_status_string(status).decode()}: {lib.svg_last_error().decode()}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else _c_vp(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return _c_vp(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _check_qkv(name: str, t: torch.Tensor, shape, dtype=torch.bfloat16, device=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def geometry(x: torch.Tensor, F: int, HH: int, WW: int) -> Geom:
+    """The svg_geom of a [B, H, S, D] tensor laid out on an F x HH x WW token grid."""
+    if x.dim() != 4:
+        raise ValueError("expected a [B, H, S, D] tensor")
+    B, H, S, D = x.shape
+    if S != F * HH * WW:
+        raise ValueError(f"S={S} does not equal F*HH*WW={F * HH * WW}")
+    return Geom(B, H, F, HH, WW, D)
+
+
+def _shape(g: Geom):
+    return (g.B, g.H, g.F * g.HH * g.WW, g.D)
+
+
+def default_scale(D: int) -> float:
+    return 1.0 / math.sqrt(D)
+
+
+def rope_split(D: int) -> Tuple[int, int, int]:
+    """Frame / row / column slice widths of the head dim: D - 4*floor(D/6), 2*floor(D/6), 2*floor(D/6)."""
+    third = 2 * (D // 6)
+    return D - 2 * third, third, third
+
+
+def workspace_bytes(op: int, g: Geom, n_q: int = 0) -> int:
+    return int(lib.svg_workspace_bytes(op, ctypes.byref(g), n_q))
+
+
+def tile_shape() -> Tuple[int, int]:
+    bm, bn = _c_i32(), _c_i32()
+    lib.svg_tile_shape(ctypes.byref(bm), ctypes.byref(bn))
+    return bm.value, bn.value
+
+
+def _workspace(op: int, g: Geom, n_q: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
+    need = workspace_bytes(op, g, n_q)
+    if ws is None:
+        return torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    if ws.dtype != torch.uint8 or ws.device != device or not ws.is_contiguous() or ws.numel() < need:
+        raise ValueError(f"workspace must be a contiguous uint8 tensor of >= {need} bytes on {device}")
+    return ws
+
+
+def qknorm_rope(q, k, wq, wk, F, HH, WW, eps=1e-6, rope_base=10000.0, dims=None, q_out=None, k_out=None):
+    """QK-RMSNorm + 3D RoPE of q and k (svg_qknorm_rope). Returns (q_out, k_out)."""
+    g = geometry(q, F, HH, WW)
+    shp = _shape(g)
+    _check_qkv("q", q, shp)
+    _check_qkv("k", k, shp, device=q.device)
+    _check_qkv("wq", wq, (g.D,), torch.float32, q.device)
+    _check_qkv("wk", wk, (g.D,), torch.float32, q.device)
+    q_out = torch.empty_like(q) if q_out is None else q_out
+    k_out = torch.empty_like(k) if k_out is None else k_out
+    _check_qkv("q_out", q_out, shp, device=q.device)
+    _check_qkv("k_out", k_out, shp, device=q.device)
+    dt, dh, dw = rope_split(g.D) if dims is None else dims
+    _check(lib.svg_qknorm_rope(_ptr(q), _ptr(k), _ptr(q_out), _ptr(k_out), _ptr(wq), _ptr(wk), float(eps),
+                               float(rope_base), dt, dh, dw, g, _stream(q)))
+    return q_out, k_out
+
+
+def profile_heads(q, k, v, q_idx, F, HH, WW, w_f, w_p, scale=None, mse=None, kind=None, ws=None):
+    """Per-head spatial/temporal choice from sampled query rows (svg_profile_heads).
+
+    q_idx: int32 [n_q] device tensor of frame-major rows.  Returns (mse [B, H, 2] fp32,
+    kind [B, H] uint8).
+    """
+    g = geometry(q, F, HH, WW)
+    shp = _shape(g)
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check_qkv(n, t, shp, device=q.device)
+    if q_idx.dtype != torch.int32 or q_idx.dim() != 1 or q_idx.device != q.device or not q_idx.is_contiguous():
+        raise ValueError("q_idx must be a contiguous int32 [n_q] tensor on the same device")
+    n_q = q_idx.numel()
+    mse = torch.empty((g.B, g.H, 2), dtype=torch.float32, device=q.device) if mse is None else mse
+    kind = torch.empty((g.B, g.H), dtype=torch.uint8, device=q.device) if kind is None else kind
+    _check_qkv("mse", mse, (g.B, g.H, 2), torch.float32, q.device)
+    _check_qkv("kind", kind, (g.B, g.H), torch.uint8, q.device)
+    ws = _workspace(OP_PROFILE, g, n_q, q.device, ws)
+    sc = default_scale(g.D) if scale is None else scale
+    _check(lib.svg_profile_heads(_ptr(q), _ptr(k), _ptr(v), _ptr(q_idx), n_q, g, Windows(w_f, w_p), float(sc),
+                                 _ptr(mse), _ptr(kind), _ptr(ws), ws.numel(), _stream(q)))
+    return mse, kind
+
+
+def _perm(fn, x, F, HH, WW, kind, select, out):
+    g = geometry(x, F, HH, WW)
+    if x.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("permute supports bf16 and fp32 rows")
+    _check_qkv("x", x, _shape(g), x.dtype)
+    out = torch.empty_like(x) if out is None else out
+    _check_qkv("out", out, _shape(g), x.dtype, x.device)
+    if kind is not None:
+        _check_qkv("kind", kind, (g.B, g.H), torch.uint8, x.device)
+    fn(_ptr(x), _ptr(out), x.element_size(), _ptr(kind), int(select), g, _stream(x))
+    return out
+
+
+def permute(x, F, HH, WW, kind=None, select=TEMPORAL, out=None):
+    """Frame-major -> token-major (svg_permute) for heads with kind == select (all if kind is None)."""
+    return _perm(lambda *a: _check(lib.svg_permute(*a)), x, F, HH, WW, kind, select, out)
+
+
+def unpermute(x, F, HH, WW, kind=None, select=TEMPORAL, out=None):
+    """Token-major -> frame-major (svg_unpermute) for heads with kind == select (all if kind is None)."""
+    return _perm(lambda *a: _check(lib.svg_unpermute(*a)), x, F, HH, WW, kind, select, out)
+
+
+def build_block_mask(kind, F, HH, WW, w_f, w_p, bm, bn):
+    """uint8 [B, H, ceil(S/bm), ceil(S/bn)] tile mask in each head's layout (svg_build_block_mask)."""
+    if kind.dtype != torch.uint8 or kind.dim() != 2 or kind.device.type != "cuda" or not kind.is_contiguous():
+        raise ValueError("kind must be a contiguous uint8 [B, H] device tensor")
+    B, H = kind.shape
+    g = Geom(B, H, F, HH, WW, 64)
+    S = F * HH * WW
+    out = torch.empty((B, H, -(-S // bm), -(-S // bn)), dtype=torch.uint8, device=kind.device)
+    _check(lib.svg_build_block_mask(_ptr(kind), g, Windows(w_f, w_p), bm, bn, _ptr(out), _stream(kind)))
+    return out
+
+
+def sparse_attn(q, k, v, qt, kt, vt, kind, F, HH, WW, w_f, w_p, scale=None, o=None, ot=None, ws=None):
+    """Block-sparse attention (svg_sparse_attn): spatial/dense heads read q/k/v and write o
+    (frame-major); temporal heads read qt/kt/vt and write ot (token-major).  Returns (o, ot)."""
+    g = geometry(q, F, HH, WW)
+    shp = _shape(g)
+    for n, t in (("q", q), ("k", k), ("v", v), ("qt", qt), ("kt", kt), ("vt", vt)):
+        _check_qkv(n, t, shp, device=q.device)
+    _check_qkv("kind", kind, (g.B, g.H), torch.uint8, q.device)
+    o = torch.empty_like(q) if o is None else o
+    ot = torch.empty_like(q) if ot is None else ot
+    _check_qkv("o", o, shp, device=q.device)
+    _check_qkv("ot", ot, shp, device=q.device)
+    ws = _workspace(OP_SPARSE_ATTN, g, 0, q.device, ws)
+    sc = default_scale(g.D) if scale is None else scale
+    _check(lib.svg_sparse_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(qt), _ptr(kt), _ptr(vt), _ptr(kind), g,
+                               Windows(w_f, w_p), float(sc), _ptr(o), _ptr(ot), _ptr(ws), ws.numel(), _stream(q)))
+    return o, ot
+
+
+def dense_attn(q, k, v, F, HH, WW, scale=None, o=None):
+    """Unmasked attention with the same kernel (svg_dense_attn)."""
+    g = geometry(q, F, HH, WW)
+    shp = _shape(g)
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check_qkv(n, t, shp, device=q.device)
+    o = torch.empty_like(q) if o is None else o
+    _check_qkv("o", o, shp, device=q.device)
+    sc = default_scale(g.D) if scale is None else scale
+    _check(lib.svg_dense_attn(_ptr(q), _ptr(k), _ptr(v), g, float(sc), _ptr(o), _stream(q)))
+    return o
+
+
+class LayerBuffers:
+    """Device buffers one sparse layer reuses across calls (token-major copies, outputs, workspaces)."""
+
+    def __init__(self, like: torch.Tensor, n_q: int, F: int, HH: int, WW: int):
+        g = geometry(like, F, HH, WW)
+        dev = like.device
+        self.qt, self.kt, self.vt, self.ot = (torch.empty_like(like) for _ in range(4))
+        self.o = torch.empty_like(like)
+        self.qn = torch.empty_like(like)
+        self.kn = torch.empty_like(like)
+        self.mse = torch.empty((g.B, g.H, 2), dtype=torch.float32, device=dev)
+        self.kind = torch.empty((g.B, g.H), dtype=torch.uint8, device=dev)
+        self.ws_profile = torch.empty(max(256, workspace_bytes(OP_PROFILE, g, n_q)), dtype=torch.uint8, device=dev)
+        self.ws_attn = torch.empty(max(256, workspace_bytes(OP_SPARSE_ATTN, g, 0)), dtype=torch.uint8, device=dev)
+
+
+def sparse_layer(q, k, v, q_idx, F, HH, WW, w_f, w_p, norm=None, scale=None, bufs: Optional[LayerBuffers] = None):
+    """One layer of the path, all on the current stream with no host synchronisation:
+    [QK-RMSNorm + 3D RoPE] -> profile heads -> token-major copies of temporal heads' Q/K/V ->
+    block-sparse attention -> frame-major output.
+
+    norm: None or (wq, wk, eps, rope_base).  Returns (o, kind, mse, q', k').
+    """
+    if bufs is None:
+        bufs = LayerBuffers(q, q_idx.numel(), F, HH, WW)
+    if norm is not None:
+        wq, wk, eps, base = norm
+        q, k = qknorm_rope(q, k, wq, wk, F, HH, WW, eps, base, q_out=bufs.qn, k_out=bufs.kn)
+    profile_heads(q, k, v, q_idx, F, HH, WW, w_f, w_p, scale, mse=bufs.mse, kind=bufs.kind, ws=bufs.ws_profile)
+    permute(q, F, HH, WW, bufs.kind, TEMPORAL, out=bufs.qt)
+    permute(k, F, HH, WW, bufs.kind, TEMPORAL, out=bufs.kt)
+    permute(v, F, HH, WW, bufs.kind, TEMPORAL, out=bufs.vt)
+    sparse_attn(q, k, v, bufs.qt, bufs.kt, bufs.vt, bufs.kind, F, HH, WW, w_f, w_p, scale, o=bufs.o, ot=bufs.ot,
+                ws=bufs.ws_attn)
+    unpermute(bufs.ot, F, HH, WW, bufs.kind, TEMPORAL, out=bufs.o)
+    return bufs.o, bufs.kind, bufs.mse, q, k

@@ -1,0 +1,324 @@
+// C ABI of libsvg: argument checks, workspace sizing and kernel launches.  Every argument
+// is validated on the host before anything is enqueued; HIP launch errors map to
+// SVG_ERR_HIP.  Nothing here allocates device memory or synchronises the host.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/svg.h"
+#include "svg_internal.h"
+
+#define SVG_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_last_error;
+
+svg_status fail(svg_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+svg_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return SVG_OK;
+  return fail(SVG_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Geometry checks shared by every call.  `need_d` requires D in {64, 128}.
+svg_status check_geom(const svg_geom& g, bool need_d) {
+  if (g.B <= 0 || g.H <= 0 || g.F <= 0 || g.HH <= 0 || g.WW <= 0 || g.D <= 0)
+    return fail(SVG_ERR_INVALID, "geometry fields must be > 0 (B=%d H=%d F=%d HH=%d WW=%d D=%d)", g.B, g.H, g.F, g.HH,
+                g.WW, g.D);
+  const int64_t P = (int64_t)g.HH * g.WW;
+  const int64_t S = P * g.F;
+  if (S >= (int64_t)1 << 30) return fail(SVG_ERR_INVALID, "S = F*HH*WW = %lld is too large", (long long)S);
+  const int64_t BH = (int64_t)g.B * g.H;
+  if (BH >= (int64_t)1 << 24) return fail(SVG_ERR_INVALID, "B*H = %lld is too large", (long long)BH);
+  if (BH * S >= (int64_t)1 << 31)
+    return fail(SVG_ERR_INVALID, "B*H*S = %lld rows exceeds 2^31", (long long)(BH * S));
+  if (need_d && g.D != 64 && g.D != 128) return fail(SVG_ERR_UNSUPPORTED, "head dim D=%d: only 64 and 128 are built", g.D);
+  return SVG_OK;
+}
+
+svg_status check_windows(const svg_windows& w) {
+  if (w.frames < 0 || w.positions < 0)
+    return fail(SVG_ERR_INVALID, "windows must be >= 0 (frames=%d positions=%d)", w.frames, w.positions);
+  return SVG_OK;
+}
+
+svg_status check_ptrs(std::initializer_list<std::pair<const void*, const char*>> ps) {
+  for (auto& p : ps) {
+    if (p.first == nullptr) return fail(SVG_ERR_INVALID, "%s is NULL", p.second);
+    if (!aligned16(p.first)) return fail(SVG_ERR_INVALID, "%s is not 16-byte aligned", p.second);
+  }
+  return SVG_OK;
+}
+
+int32_t clamp_window(int32_t w, int32_t n) { return w > n ? n : w; }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+size_t profile_ws_bytes(const svg_geom& g, int32_t n_q) {
+  const int32_t S = g.F * g.HH * g.WW;
+  svg::ProfilePlan p = svg::profile_plan(g.B * g.H, S, g.D, n_q);
+  return align_up(p.ml_floats * sizeof(float), 256) + align_up(p.o_floats * sizeof(float), 256);
+}
+
+size_t attn_ws_bytes(const svg_geom& g) { return align_up((size_t)g.B * g.H * sizeof(int32_t), 256); }
+
+}  // namespace
+
+SVG_API svg_status svg_qknorm_rope(const void* q, const void* k, void* q_out, void* k_out, const float* wq,
+                                   const float* wk, float eps, float rope_base, int32_t dt, int32_t dh, int32_t dw,
+                                   svg_geom g, void* stream) {
+  svg_status s;
+  if ((s = check_geom(g, true)) != SVG_OK) return s;
+  if ((s = check_ptrs({{q, "q"}, {k, "k"}, {q_out, "q_out"}, {k_out, "k_out"}, {wq, "wq"}, {wk, "wk"}})) != SVG_OK)
+    return s;
+  if (!(eps > 0.f) || !std::isfinite(eps)) return fail(SVG_ERR_INVALID, "eps must be finite and > 0");
+  if (!(rope_base > 0.f) || !std::isfinite(rope_base)) return fail(SVG_ERR_INVALID, "rope_base must be finite and > 0");
+  if (dt < 0 || dh < 0 || dw < 0 || (dt & 1) || (dh & 1) || (dw & 1) || dt + dh + dw != g.D)
+    return fail(SVG_ERR_INVALID, "rope slices dt=%d dh=%d dw=%d must be even, >= 0 and sum to D=%d", dt, dh, dw, g.D);
+  const int64_t entries = (int64_t)g.F * (dt / 2) + (int64_t)g.HH * (dh / 2) + (int64_t)g.WW * (dw / 2);
+  if (entries * 8 > 64 * 1024)
+    return fail(SVG_ERR_UNSUPPORTED, "rope tables (%lld entries) exceed 64 KiB of LDS", (long long)entries);
+  svg::RopeArgs a;
+  a.in[0] = (const svg::bf16*)q;
+  a.in[1] = (const svg::bf16*)k;
+  a.out[0] = (svg::bf16*)q_out;
+  a.out[1] = (svg::bf16*)k_out;
+  a.w[0] = wq;
+  a.w[1] = wk;
+  a.eps = eps;
+  a.base = (double)rope_base;
+  a.BH = g.B * g.H;
+  a.S = g.F * g.HH * g.WW;
+  a.F = g.F;
+  a.HH = g.HH;
+  a.WW = g.WW;
+  a.P = g.HH * g.WW;
+  a.D = g.D;
+  a.dt = dt;
+  a.dh = dh;
+  a.dw = dw;
+  a.divS = svg::make_fastdiv((uint32_t)a.S);
+  a.divP = svg::make_fastdiv((uint32_t)(g.HH * g.WW));
+  a.divWW = svg::make_fastdiv((uint32_t)g.WW);
+  return hip_status(svg::launch_qknorm_rope(a, (hipStream_t)stream), "svg_qknorm_rope");
+}
+
+SVG_API svg_status svg_profile_heads(const void* q, const void* k, const void* v, const int32_t* q_idx, int32_t n_q,
+                                     svg_geom g, svg_windows w, float scale, float* mse_out, uint8_t* kind_out,
+                                     void* ws, size_t ws_bytes, void* stream) {
+  svg_status s;
+  if ((s = check_geom(g, true)) != SVG_OK) return s;
+  if ((s = check_windows(w)) != SVG_OK) return s;
+  if ((s = check_ptrs({{q, "q"}, {k, "k"}, {v, "v"}})) != SVG_OK) return s;
+  if (q_idx == nullptr || mse_out == nullptr || kind_out == nullptr)
+    return fail(SVG_ERR_INVALID, "q_idx, mse_out and kind_out must not be NULL");
+  if (((uintptr_t)q_idx & 3u) || ((uintptr_t)mse_out & 3u))
+    return fail(SVG_ERR_INVALID, "q_idx and mse_out must be 4-byte aligned");
+  const int32_t S = g.F * g.HH * g.WW;
+  if (n_q < 1 || n_q > S) return fail(SVG_ERR_INVALID, "n_q=%d must be in [1, S=%d]", n_q, S);
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(SVG_ERR_INVALID, "scale must be finite and > 0");
+  const size_t need = profile_ws_bytes(g, n_q);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(SVG_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws == nullptr ? (size_t)0 : ws_bytes);
+  if (!aligned16(ws)) return fail(SVG_ERR_INVALID, "ws is not 16-byte aligned");
+  svg::ProfilePlan plan = svg::profile_plan(g.B * g.H, S, g.D, n_q);
+  svg::ProfileArgs a;
+  a.q = (const svg::bf16*)q;
+  a.k = (const svg::bf16*)k;
+  a.v = (const svg::bf16*)v;
+  a.idx = q_idx;
+  a.n_q = n_q;
+  a.n_zq = plan.n_zq;
+  a.BH = g.B * g.H;
+  a.S = S;
+  a.F = g.F;
+  a.P = g.HH * g.WW;
+  a.D = g.D;
+  a.w_f = clamp_window(w.frames, g.F);
+  a.w_p = clamp_window(w.positions, a.P);
+  a.divP = svg::make_fastdiv((uint32_t)a.P);
+  a.scale = scale;
+  a.nsplit = plan.nsplit;
+  a.keys_per_split = plan.keys_per_split;
+  a.part_ml = (float*)ws;
+  a.part_o = (float*)((char*)ws + align_up(plan.ml_floats * sizeof(float), 256));
+  a.mse = mse_out;
+  a.kind = kind_out;
+  return hip_status(svg::launch_profile(a, (hipStream_t)stream), "svg_profile_heads");
+}
+
+static svg_status permute_common(const void* src, void* dst, int32_t elem_bytes, const uint8_t* kind, int32_t select,
+                                 svg_geom g, void* stream, bool inverse) {
+  svg_status s;
+  if ((s = check_geom(g, false)) != SVG_OK) return s;
+  if ((s = check_ptrs({{src, "src"}, {dst, "dst"}})) != SVG_OK) return s;
+  if (elem_bytes != 2 && elem_bytes != 4) return fail(SVG_ERR_INVALID, "elem_bytes=%d must be 2 or 4", elem_bytes);
+  const int64_t row_bytes = (int64_t)g.D * elem_bytes;
+  if (row_bytes != 128 && row_bytes != 256 && row_bytes != 512)
+    return fail(SVG_ERR_UNSUPPORTED, "row of D*elem_bytes=%lld bytes: 128, 256 or 512 supported", (long long)row_bytes);
+  const int32_t S = g.F * g.HH * g.WW;
+  const size_t bytes = (size_t)g.B * g.H * S * row_bytes;
+  const char* a0 = (const char*)src;
+  const char* b0 = (const char*)dst;
+  if (a0 < b0 + bytes && b0 < a0 + bytes) return fail(SVG_ERR_INVALID, "src and dst overlap");
+  svg::PermuteArgs a;
+  a.src = src;
+  a.dst = dst;
+  a.kind = kind;
+  a.select = select;
+  a.BH = g.B * g.H;
+  a.S = S;
+  a.row_bytes = (int32_t)row_bytes;
+  const int32_t P = g.HH * g.WW;
+  a.divA = svg::make_fastdiv((uint32_t)(inverse ? P : g.F));
+  a.Bm = inverse ? g.F : P;
+  return hip_status(svg::launch_permute(a, (hipStream_t)stream), inverse ? "svg_unpermute" : "svg_permute");
+}
+
+SVG_API svg_status svg_permute(const void* src, void* dst, int32_t elem_bytes, const uint8_t* kind, int32_t select,
+                               svg_geom g, void* stream) {
+  return permute_common(src, dst, elem_bytes, kind, select, g, stream, false);
+}
+
+SVG_API svg_status svg_unpermute(const void* src, void* dst, int32_t elem_bytes, const uint8_t* kind, int32_t select,
+                                 svg_geom g, void* stream) {
+  return permute_common(src, dst, elem_bytes, kind, select, g, stream, true);
+}
+
+SVG_API svg_status svg_build_block_mask(const uint8_t* kind, svg_geom g, svg_windows w, int32_t bm, int32_t bn,
+                                        uint8_t* mask_out, void* stream) {
+  svg_status s;
+  if ((s = check_geom(g, false)) != SVG_OK) return s;
+  if ((s = check_windows(w)) != SVG_OK) return s;
+  if (kind == nullptr || mask_out == nullptr) return fail(SVG_ERR_INVALID, "kind and mask_out must not be NULL");
+  const int32_t S = g.F * g.HH * g.WW;
+  if (bm < 1 || bn < 1 || bm > (1 << 30) || bn > (1 << 30))
+    return fail(SVG_ERR_INVALID, "bm=%d, bn=%d must be in [1, 2^30]", bm, bn);
+  svg::BlockMaskArgs a;
+  a.kind = kind;
+  a.out = mask_out;
+  a.BH = g.B * g.H;
+  a.S = S;
+  a.F = g.F;
+  a.P = g.HH * g.WW;
+  a.w_f = clamp_window(w.frames, g.F);
+  a.w_p = clamp_window(w.positions, a.P);
+  a.bm = bm;
+  a.bn = bn;
+  a.nqb = (S + bm - 1) / bm;
+  a.nkb = (S + bn - 1) / bn;
+  a.divP = svg::make_fastdiv((uint32_t)a.P);
+  a.divF = svg::make_fastdiv((uint32_t)g.F);
+  return hip_status(svg::launch_block_mask(a, (hipStream_t)stream), "svg_build_block_mask");
+}
+
+static void fill_attn(svg::AttnArgs& a, svg_geom g, svg_windows w, float scale) {
+  a.BH = g.B * g.H;
+  a.S = g.F * g.HH * g.WW;
+  a.F = g.F;
+  a.P = g.HH * g.WW;
+  a.D = g.D;
+  a.w_f = clamp_window(w.frames, g.F);
+  a.w_p = clamp_window(w.positions, a.P);
+  a.divP = svg::make_fastdiv((uint32_t)a.P);
+  a.divF = svg::make_fastdiv((uint32_t)g.F);
+  a.scale = scale;
+}
+
+SVG_API svg_status svg_sparse_attn(const void* q, const void* k, const void* v, const void* qt, const void* kt,
+                                   const void* vt, const uint8_t* kind, svg_geom g, svg_windows w, float scale, void* o,
+                                   void* ot, void* ws, size_t ws_bytes, void* stream) {
+  svg_status s;
+  if ((s = check_geom(g, true)) != SVG_OK) return s;
+  if ((s = check_windows(w)) != SVG_OK) return s;
+  if ((s = check_ptrs({{q, "q"}, {k, "k"}, {v, "v"}, {o, "o"}})) != SVG_OK) return s;
+  if (kind != nullptr) {
+    if ((s = check_ptrs({{qt, "qt"}, {kt, "kt"}, {vt, "vt"}, {ot, "ot"}})) != SVG_OK) return s;
+  }
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(SVG_ERR_INVALID, "scale must be finite and > 0");
+  const size_t need = attn_ws_bytes(g);
+  if (kind != nullptr && (ws == nullptr || ws_bytes < need))
+    return fail(SVG_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws == nullptr ? (size_t)0 : ws_bytes);
+  if (kind != nullptr && ((uintptr_t)ws & 3u)) return fail(SVG_ERR_INVALID, "ws is not 4-byte aligned");
+  svg::AttnArgs a;
+  a.q = (const svg::bf16*)q;
+  a.k = (const svg::bf16*)k;
+  a.v = (const svg::bf16*)v;
+  a.qt = (const svg::bf16*)(qt ? qt : q);
+  a.kt = (const svg::bf16*)(kt ? kt : k);
+  a.vt = (const svg::bf16*)(vt ? vt : v);
+  a.o = (svg::bf16*)o;
+  a.ot = (svg::bf16*)(ot ? ot : o);
+  a.kind = kind;
+  a.order = kind ? (int32_t*)ws : nullptr;
+  a.force_dense = 0;
+  fill_attn(a, g, w, scale);
+  return hip_status(svg::launch_attention(a, (hipStream_t)stream), "svg_sparse_attn");
+}
+
+SVG_API svg_status svg_dense_attn(const void* q, const void* k, const void* v, svg_geom g, float scale, void* o,
+                                  void* stream) {
+  svg_status s;
+  if ((s = check_geom(g, true)) != SVG_OK) return s;
+  if ((s = check_ptrs({{q, "q"}, {k, "k"}, {v, "v"}, {o, "o"}})) != SVG_OK) return s;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(SVG_ERR_INVALID, "scale must be finite and > 0");
+  svg::AttnArgs a;
+  a.q = a.qt = (const svg::bf16*)q;
+  a.k = a.kt = (const svg::bf16*)k;
+  a.v = a.vt = (const svg::bf16*)v;
+  a.o = a.ot = (svg::bf16*)o;
+  a.kind = nullptr;
+  a.order = nullptr;
+  a.force_dense = 1;
+  fill_attn(a, g, svg_windows{0, 0}, scale);
+  return hip_status(svg::launch_attention(a, (hipStream_t)stream), "svg_dense_attn");
+}
+
+SVG_API size_t svg_workspace_bytes(int32_t op, const svg_geom* g, int32_t n_q) {
+  if (g == nullptr) return 0;
+  const bool need_d = true;
+  std::string saved = g_last_error;
+  const bool good = check_geom(*g, need_d) == SVG_OK;
+  g_last_error = saved;
+  if (!good) return 0;
+  if (op == SVG_OP_PROFILE) {
+    const int32_t S = g->F * g->HH * g->WW;
+    if (n_q < 1 || n_q > S) return 0;
+    return profile_ws_bytes(*g, n_q);
+  }
+  if (op == SVG_OP_SPARSE_ATTN) return attn_ws_bytes(*g);
+  return 0;
+}
+
+SVG_API void svg_tile_shape(int32_t* bm, int32_t* bn) {
+  if (bm) *bm = svg::ATTN_BM;
+  if (bn) *bn = svg::ATTN_BN;
+}
+
+SVG_API const char* svg_status_string(svg_status s) {
+  switch (s) {
+    case SVG_OK: return "SVG_OK: success";
+    case SVG_ERR_INVALID: return "SVG_ERR_INVALID: invalid argument";
+    case SVG_ERR_UNSUPPORTED: return "SVG_ERR_UNSUPPORTED: request not supported by this build";
+    case SVG_ERR_HIP: return "SVG_ERR_HIP: HIP runtime error";
+    case SVG_ERR_WORKSPACE: return "SVG_ERR_WORKSPACE: workspace missing or too small";
+    default: return "unknown svg_status";
+  }
+}
+
+SVG_API const char* svg_last_error(void) { return g_last_error.c_str(); }

@@ -1,0 +1,54 @@
+// Layout transformation between frame-major and token-major order (a transpose of the
+// frame x location grid of each head), after the Sparse VideoGen authors' article,
+// section "Layout Transformation", and 机器之心's article, layout section.
+//
+// Both directions are row gathers: dst row r <- src row (r mod A) * Bm + r div A, with
+// (A, Bm) = (F, P) for frame->token-major and (P, F) for token->frame-major.  Each row is
+// D * elem_bytes bytes (128..512), copied as 16-byte vectors; destination writes are fully
+// contiguous, source reads are whole rows (>= 128 contiguous bytes each).  HBM-bound.
+#include "svg_internal.h"
+
+namespace svg {
+
+namespace {
+
+constexpr int PERM_THREADS = 256;
+constexpr int PERM_ROWS_PER_BLOCK = 64;
+
+template <int CPR>  // 16-byte chunks per row
+__global__ __launch_bounds__(PERM_THREADS) void permute_rows_kernel(PermuteArgs a, int32_t blocks_per_head) {
+  const int32_t bh = blockIdx.x / blocks_per_head;
+  const int32_t rb = blockIdx.x - bh * blocks_per_head;
+  if (a.kind != nullptr && (int32_t)a.kind[bh] != a.select) return;
+  const size_t head_off = (size_t)bh * (size_t)a.S * (size_t)CPR;  // in 16-byte chunks
+  const u32x4* __restrict__ src = reinterpret_cast<const u32x4*>(a.src) + head_off;
+  u32x4* __restrict__ dst = reinterpret_cast<u32x4*>(a.dst) + head_off;
+  constexpr int ROWS_PER_PASS = PERM_THREADS / CPR;
+  const int32_t c = threadIdx.x % CPR;
+  const int32_t r0 = rb * PERM_ROWS_PER_BLOCK + threadIdx.x / CPR;
+#pragma unroll
+  for (int i = 0; i < PERM_ROWS_PER_BLOCK / ROWS_PER_PASS; ++i) {
+    const int32_t r = r0 + i * ROWS_PER_PASS;
+    if (r < a.S) {
+      const uint32_t q = fdiv((uint32_t)r, a.divA);
+      const int32_t s = (int32_t)((uint32_t)r - q * a.divA.d) * a.Bm + (int32_t)q;
+      dst[(size_t)r * CPR + c] = src[(size_t)s * CPR + c];
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t st) {
+  const int32_t bph = (a.S + PERM_ROWS_PER_BLOCK - 1) / PERM_ROWS_PER_BLOCK;
+  const dim3 grid((unsigned)((int64_t)bph * a.BH));
+  switch (a.row_bytes / 16) {
+    case 8: permute_rows_kernel<8><<<grid, PERM_THREADS, 0, st>>>(a, bph); break;
+    case 16: permute_rows_kernel<16><<<grid, PERM_THREADS, 0, st>>>(a, bph); break;
+    case 32: permute_rows_kernel<32><<<grid, PERM_THREADS, 0, st>>>(a, bph); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace svg

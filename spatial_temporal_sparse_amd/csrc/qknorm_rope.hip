@@ -1,0 +1,135 @@
+// Fused QK-RMSNorm + 3D rotary embedding of Q and K.  The Sparse VideoGen pages name both
+// operations as a cost worth a custom kernel (authors' article, closing "other
+// optimisations" section; 机器之心 article, end of the layout section) without defining
+// them; this kernel computes, per row of D channels,
+//   y = x / sqrt(mean(x^2) + eps) * w,   then rotates channel pairs (2j, 2j+1) of the
+//   frame / grid-row / grid-column slice (widths dt, dh, dw) by pos * base^(-2j/n).
+//
+// HBM-bound: each row is read once and written once (2 x D x 2 bytes), everything else is
+// register or LDS work.  D/8 lanes own a row (8 channels = one 16-byte vector each); the
+// sum of squares is reduced across those lanes with cross-lane shuffles.  The cos/sin of
+// every (axis, position, pair) -- F*dt/2 + HH*dh/2 + WW*dw/2 entries -- are computed once
+// per block in fp64 and kept in LDS as fp32 pairs, so no transcendental runs per element.
+#include "svg_internal.h"
+
+namespace svg {
+
+namespace {
+
+constexpr int ROPE_THREADS = 256;
+constexpr int ROPE_UNROLL = 4;     // rows in flight per lane
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t h) {
+  return __uint_as_float(h << 16);
+}
+
+template <int D>
+__global__ __launch_bounds__(ROPE_THREADS) void qknorm_rope_kernel(RopeArgs a) {
+  extern __shared__ float2 tab[];
+  constexpr int LPR = D / 8;                 // lanes per row
+  constexpr int RPP = ROPE_THREADS / LPR;    // rows per pass of the block
+  const int which = blockIdx.y;              // 0: Q, 1: K
+  const int tid = threadIdx.x;
+
+  // ---- per-block cos/sin tables (fp64 angle and sincos, stored as fp32) ----
+  const int nt = a.dt / 2, nh = a.dh / 2, nw = a.dw / 2;
+  const int Et = a.F * nt, Eh = a.HH * nh, Ew = a.WW * nw;
+  for (int e = tid; e < Et + Eh + Ew; e += ROPE_THREADS) {
+    int pos, j, n;
+    if (e < Et) { pos = e / nt; j = e - pos * nt; n = a.dt; }
+    else if (e < Et + Eh) { const int r = e - Et; pos = r / nh; j = r - pos * nh; n = a.dh; }
+    else { const int r = e - Et - Eh; pos = r / nw; j = r - pos * nw; n = a.dw; }
+    const double theta = (double)pos * pow(a.base, -2.0 * (double)j / (double)n);
+    double s, c;
+    sincos(theta, &s, &c);
+    tab[e] = make_float2((float)c, (float)s);
+  }
+
+  // ---- this lane's four channel pairs: table base and per-position stride ----
+  const int lane_c = tid % LPR;
+  int tab_base[4], tab_stride[4], axis[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int pp = lane_c * 4 + i;
+    if (pp < nt) { axis[i] = 0; tab_base[i] = pp; tab_stride[i] = nt; }
+    else if (pp < nt + nh) { axis[i] = 1; tab_base[i] = Et + (pp - nt); tab_stride[i] = nh; }
+    else { axis[i] = 2; tab_base[i] = Et + Eh + (pp - nt - nh); tab_stride[i] = nw; }
+  }
+  float w[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) w[c] = a.w[which][lane_c * 8 + c];
+  __syncthreads();
+
+  const u32x4* __restrict__ in = reinterpret_cast<const u32x4*>(a.in[which]);
+  u32x4* __restrict__ out = reinterpret_cast<u32x4*>(a.out[which]);
+  const int64_t total = (int64_t)a.BH * a.S;
+  const int64_t stride = (int64_t)gridDim.x * RPP;
+  const float inv_d = 1.0f / (float)D;
+
+  for (int64_t base = (int64_t)blockIdx.x * RPP + tid / LPR; base < total; base += stride * ROPE_UNROLL) {
+    u32x4 raw[ROPE_UNROLL];
+#pragma unroll
+    for (int u = 0; u < ROPE_UNROLL; ++u) {
+      const int64_t row = base + u * stride;
+      if (row < total) raw[u] = in[row * LPR + lane_c];
+    }
+#pragma unroll
+    for (int u = 0; u < ROPE_UNROLL; ++u) {
+      const int64_t row = base + u * stride;
+      // every lane of a row takes the same branch, so the shuffles below see whole rows
+      if (row >= total) break;
+      float x[8];
+      const u32x4 wd = raw[u];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        x[2 * c] = bf16_bits_to_float(wd[c] & 0xffffu);
+        x[2 * c + 1] = bf16_bits_to_float(wd[c] >> 16);
+      }
+      float ss = 0.f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) ss = fmaf(x[c], x[c], ss);
+#pragma unroll
+      for (int m = LPR / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+      const float rs = rsqrtf(ss * inv_d + a.eps);
+
+      const uint32_t tok = (uint32_t)(row - (int64_t)fdiv((uint32_t)row, a.divS) * a.S);
+      const uint32_t f = fdiv(tok, a.divP);
+      const uint32_t p = tok - f * (uint32_t)a.P;
+      const uint32_t y = fdiv(p, a.divWW);
+      const uint32_t xx = p - y * (uint32_t)a.WW;
+
+      bf16x8 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float aa = x[2 * i] * rs * w[2 * i];
+        const float bb = x[2 * i + 1] * rs * w[2 * i + 1];
+        const int pos = axis[i] == 0 ? (int)f : (axis[i] == 1 ? (int)y : (int)xx);
+        const float2 cs = tab[tab_base[i] + pos * tab_stride[i]];
+        o[2 * i] = (bf16)(aa * cs.x - bb * cs.y);
+        o[2 * i + 1] = (bf16)(aa * cs.y + bb * cs.x);
+      }
+      out[row * LPR + lane_c] = __builtin_bit_cast(u32x4, o);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_qknorm_rope(const RopeArgs& a, hipStream_t st) {
+  const size_t lds = sizeof(float2) * (size_t)(a.F * (a.dt / 2) + a.HH * (a.dh / 2) + a.WW * (a.dw / 2));
+  const int64_t total = (int64_t)a.BH * a.S;
+  const int rpp = ROPE_THREADS / (a.D / 8);
+  int64_t blocks = (total + rpp * ROPE_UNROLL - 1) / (rpp * ROPE_UNROLL);
+  if (blocks > 2048) blocks = 2048;
+  const dim3 grid((unsigned)blocks, 2);
+  if (a.D == 128) {
+    qknorm_rope_kernel<128><<<grid, ROPE_THREADS, lds, st>>>(a);
+  } else if (a.D == 64) {
+    qknorm_rope_kernel<64><<<grid, ROPE_THREADS, lds, st>>>(a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace svg

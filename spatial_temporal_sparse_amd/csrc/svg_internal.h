@@ -1,0 +1,193 @@
+// Internal declarations shared by the HIP kernels and the C-ABI layer of libsvg.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace svg {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // 16-byte move unit
+
+constexpr int KIND_SPATIAL = 0;
+constexpr int KIND_TEMPORAL = 1;
+constexpr int KIND_DENSE = 2;
+
+// Exact unsigned division n / d for 0 <= n < 2^31 and 1 <= d < 2^31 by multiply-high
+// (Granlund & Montgomery, "Division by invariant integers using multiplication", 1994):
+// with s = ceil(log2 d) and m = floor(2^32 (2^s - d) / d) + 1, n / d = (mulhi(n, m) + n) >> s.
+struct FastDiv {
+  uint32_t d, m, s;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f;
+  f.d = d;
+  uint32_t s = 0;
+  while ((1ull << s) < d) ++s;
+  f.s = s;
+  f.m = (uint32_t)(((1ull << 32) * ((1ull << s) - d)) / d + 1);
+  return f;
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
+  return (__umulhi(n, f.m) + n) >> f.s;
+}
+__device__ __forceinline__ uint32_t fmod_(uint32_t n, const FastDiv& f) {
+  return n - fdiv(n, f) * f.d;
+}
+
+// The token mask of a head, in the head's working layout, is a band of groups: row r
+// belongs to group r / G and may attend keys of groups within +-w of it, of NG groups of
+// G tokens.  Spatial heads (frame-major): G = P, NG = F, w = w_f.  Temporal heads
+// (token-major): G = F, NG = P, w = w_p.  Each row's allowed keys therefore form one
+// contiguous interval [lo, hi) whose ends are non-decreasing in r.
+struct Band {
+  FastDiv divG;
+  int32_t G, NG, w;
+  int32_t dense;   // 1: every key of [0, S)
+  int32_t S;
+};
+
+__device__ __forceinline__ void band_interval(const Band& b, int32_t r, int32_t& lo, int32_t& hi) {
+  if (b.dense) {
+    lo = 0;
+    hi = b.S;
+    return;
+  }
+  const int32_t grp = (int32_t)fdiv((uint32_t)r, b.divG);
+  lo = max(0, grp - b.w) * b.G;
+  hi = min(b.NG, grp + b.w + 1) * b.G;
+}
+
+// ------------------------------------------------------------------------------------------
+// LDS staging helpers shared by the attention and profiling kernels.
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ i16x4 lds_read_tr(const bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+}
+
+// A operand of one O^T += V^T P^T MFMA (v_mfma_f32_32x32x16_bf16) from a row-major [key][d]
+// V tile in LDS.  The 64-bit transpose read hands lane j of each 16-lane group column j%4 of
+// the rows its group addressed; with the per-lane address p = &V[key0 + 4*h + (i>>2)][d0 +
+// 16*(g&1) + 4*(i&3)] (g = lane/16, h = g/2, i = lane%16) lane l receives V[key0 + 4h + e][d0
+// + l%32] for e = 0..3, and the second read (8 rows further) keys +8..+11.
+__device__ __forceinline__ bf16x8 load_vt(const bf16* p, int row_stride) {
+  const i16x4 lo = lds_read_tr(p);
+  const i16x4 hi = lds_read_tr(p + 8 * row_stride);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Global -> register staging of a ROWS x D tile starting at row k0 (rows clamped to S-1),
+// and register -> LDS store with row strides KS / VS, for an NTH-thread workgroup.
+template <int D, int ROWS, int NTH>
+struct TileStager {
+  static constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  static constexpr int CHUNKS = ROWS * CPR / NTH;   // per thread per tensor
+  u32x4 k[CHUNKS], v[CHUNKS];
+
+  __device__ __forceinline__ void load(const bf16* __restrict__ K, const bf16* __restrict__ V, int32_t k0, int32_t S,
+                                       int tid) {
+#pragma unroll
+    for (int i = 0; i < CHUNKS; ++i) {
+      const int c = tid + i * NTH;
+      const int row = c / CPR;
+      const int col = (c % CPR) * 8;
+      const size_t grow = (size_t)min(k0 + row, S - 1);
+      k[i] = *reinterpret_cast<const u32x4*>(K + grow * D + col);
+      v[i] = *reinterpret_cast<const u32x4*>(V + grow * D + col);
+    }
+  }
+  template <int KS, int VS>
+  __device__ __forceinline__ void store(bf16* ks, bf16* vs, int tid) const {
+#pragma unroll
+    for (int i = 0; i < CHUNKS; ++i) {
+      const int c = tid + i * NTH;
+      const int row = c / CPR;
+      const int col = (c % CPR) * 8;
+      *reinterpret_cast<u32x4*>(ks + row * KS + col) = k[i];
+      *reinterpret_cast<u32x4*>(vs + row * VS + col) = v[i];
+    }
+  }
+};
+
+// ------------------------------------------------------------------------------------------
+// Launchers (one per kernel family); each returns hipGetLastError() after enqueueing.
+// ------------------------------------------------------------------------------------------
+struct PermuteArgs {
+  const void* src;
+  void* dst;
+  const uint8_t* kind;   // may be null: every head
+  int32_t select;
+  int32_t BH, S;
+  int32_t row_bytes;     // D * elem_bytes, a multiple of 16
+  // dst row r <- src row (r mod A) * Bm + r div A
+  FastDiv divA;
+  int32_t Bm;
+};
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t st);
+
+struct BlockMaskArgs {
+  const uint8_t* kind;
+  uint8_t* out;
+  int32_t BH, S, F, P, w_f, w_p, bm, bn, nqb, nkb;
+  FastDiv divP, divF;
+};
+hipError_t launch_block_mask(const BlockMaskArgs& a, hipStream_t st);
+
+struct RopeArgs {
+  const bf16* in[2];
+  bf16* out[2];
+  const float* w[2];
+  float eps;
+  double base;
+  int32_t BH, S, F, HH, WW, P, D, dt, dh, dw;
+  FastDiv divS, divP, divWW;
+};
+hipError_t launch_qknorm_rope(const RopeArgs& a, hipStream_t st);
+
+struct AttnArgs {
+  const bf16 *q, *k, *v;      // frame-major
+  const bf16 *qt, *kt, *vt;   // token-major
+  bf16 *o, *ot;
+  const uint8_t* kind;        // null: all dense
+  int32_t* order;             // [BH] head order scratch (null: identity, no kind)
+  int32_t BH, S, F, P, D, w_f, w_p;
+  FastDiv divP, divF;
+  float scale;
+  int32_t force_dense;
+};
+hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
+
+struct ProfileArgs {
+  const bf16 *q, *k, *v;
+  const int32_t* idx;
+  int32_t n_q, n_zq;          // sampled rows; groups of 64 rows
+  int32_t BH, S, F, P, D, w_f, w_p;
+  FastDiv divP;
+  float scale;
+  int32_t nsplit, keys_per_split;
+  float* part_ml;             // [BH][2*nsplit][3][n_zq*64][2]
+  float* part_o;              // [BH][2*nsplit][3][n_zq*64][D]
+  float* mse;                 // [BH][2]
+  uint8_t* kind;              // [BH]
+};
+hipError_t launch_profile(const ProfileArgs& a, hipStream_t st);
+
+// Split-K plan of the profiling kernel, shared by the launcher and the workspace query.
+struct ProfilePlan {
+  int32_t n_zq, nsplit, keys_per_split;
+  size_t ml_floats, o_floats;
+};
+ProfilePlan profile_plan(int32_t BH, int32_t S, int32_t D, int32_t n_q);
+
+constexpr int ATTN_BM = 128;
+constexpr int ATTN_BN = 64;
+
+}  // namespace svg

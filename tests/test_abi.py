@@ -1,0 +1,116 @@
+"""The C-ABI library loads on any machine and exports exactly what include/svg.h declares.
+
+No call here reaches a kernel launch: every call carries an argument the host-side checks
+reject before anything is enqueued.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "svg.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(svg_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def svg():
+    import spatial_temporal_sparse_amd as m
+    return m
+
+
+def test_header_declares_the_path():
+    names = _declared_functions()
+    for n in ("svg_qknorm_rope", "svg_profile_heads", "svg_permute", "svg_unpermute", "svg_build_block_mask",
+              "svg_sparse_attn", "svg_dense_attn", "svg_workspace_bytes", "svg_tile_shape", "svg_status_string",
+              "svg_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(svg):
+    lib = ctypes.CDLL(svg.LIB_PATH)
+    for n in _declared_functions():
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", svg.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert set(_declared_functions()) <= exported
+    assert not [s for s in exported if s.startswith("svg_") and s not in _declared_functions()]
+
+
+def test_status_strings(svg):
+    for code, tag in ((0, "SVG_OK"), (-1, "SVG_ERR_INVALID"), (-2, "SVG_ERR_UNSUPPORTED"), (-3, "SVG_ERR_HIP"),
+                      (-4, "SVG_ERR_WORKSPACE")):
+        assert svg.lib.svg_status_string(code).decode().startswith(tag)
+    assert "unknown" in svg.lib.svg_status_string(7).decode()
+
+
+def test_tile_shape(svg):
+    assert svg.tile_shape() == (128, 64)
+
+
+def test_workspace_sizes(svg):
+    g = svg.Geom(1, 24, 33, 45, 80, 128)
+    assert svg.workspace_bytes(svg.OP_SPARSE_ATTN, g) == 256
+    ws = svg.workspace_bytes(svg.OP_PROFILE, g, 64)
+    assert ws > 0 and ws % 256 == 0
+    assert svg.workspace_bytes(svg.OP_PROFILE, g, 0) == 0                  # n_q out of range
+    assert svg.workspace_bytes(svg.OP_PROFILE, svg.Geom(1, 24, 33, 45, 80, 96), 64) == 0   # D unsupported
+    assert svg.workspace_bytes(99, g, 64) == 0
+
+
+FAKE = ctypes.c_void_p(0x100000)   # never dereferenced: each call below fails a host check first
+
+
+def test_argument_checks(svg):
+    L = svg.lib
+    W = svg.Windows
+    good = svg.Geom(1, 2, 4, 8, 8, 64)
+    # null pointers
+    assert L.svg_permute(None, FAKE, 2, None, 1, good, None) == -1
+    assert "src" in L.svg_last_error().decode()
+    # geometry fields must be positive
+    assert L.svg_permute(FAKE, ctypes.c_void_p(0x200000), 2, None, 1, svg.Geom(1, 2, 0, 8, 8, 64), None) == -1
+    # element size
+    assert L.svg_permute(FAKE, ctypes.c_void_p(0x800000), 3, None, 1, good, None) == -1
+    # misaligned pointer
+    assert L.svg_permute(ctypes.c_void_p(0x100002), ctypes.c_void_p(0x800000), 2, None, 1, good, None) == -1
+    # overlapping src / dst
+    assert L.svg_unpermute(FAKE, ctypes.c_void_p(0x100010), 2, None, 1, good, None) == -1
+    # unsupported head dim
+    assert L.svg_dense_attn(FAKE, FAKE, FAKE, svg.Geom(1, 2, 4, 8, 8, 96), 0.1, FAKE, None) == -2
+    # non-positive scale
+    assert L.svg_dense_attn(FAKE, FAKE, FAKE, good, 0.0, FAKE, None) == -1
+    # negative window
+    assert L.svg_build_block_mask(FAKE, good, W(-1, 2), 128, 64, FAKE, None) == -1
+    # empty tile
+    assert L.svg_build_block_mask(FAKE, good, W(1, 2), 0, 64, FAKE, None) == -1
+    # n_q out of range and missing workspace
+    assert L.svg_profile_heads(FAKE, FAKE, FAKE, FAKE, 0, good, W(1, 2), 0.125, FAKE, FAKE, FAKE, 1 << 30, None) == -1
+    assert L.svg_profile_heads(FAKE, FAKE, FAKE, FAKE, 64, good, W(1, 2), 0.125, FAKE, FAKE, None, 0, None) == -4
+    assert L.svg_profile_heads(FAKE, FAKE, FAKE, FAKE, 64, good, W(1, 2), 0.125, FAKE, FAKE, FAKE, 16, None) == -4
+    # sparse attention with kinds needs the token-major tensors and a workspace
+    assert L.svg_sparse_attn(FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, good, W(1, 2), 0.125, FAKE, FAKE, FAKE, 256,
+                             None) == -1
+    assert L.svg_sparse_attn(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, good, W(1, 2), 0.125, FAKE, FAKE, None, 0,
+                             None) == -4
+    # rope slices must be even and add up to D; eps must be positive
+    assert L.svg_qknorm_rope(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1e-6, 1e4, 24, 21, 19, good, None) == -1
+    assert L.svg_qknorm_rope(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.0, 1e4, 24, 20, 20, good, None) == -1
+    # sequence too long
+    assert L.svg_dense_attn(FAKE, FAKE, FAKE, svg.Geom(1, 1, 1 << 16, 1 << 8, 1 << 8, 64), 0.1, FAKE, None) == -1
+
+
+def test_binding_rejects_host_tensors(svg):
+    import torch
+    x = torch.zeros((1, 2, 256, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        svg.permute(x, 4, 8, 8)
+    with pytest.raises(ValueError):
+        svg.geometry(x, 4, 8, 9)

@@ -1,0 +1,79 @@
+"""One full layer of the path on the GPU against the oracle, stage by stage.
+
+Each stage is compared on the exact bf16 values the GPU stage consumed: norm/RoPE on the
+layer inputs, profiling and attention on the GPU's normalised Q/K (bf16) and V.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle.svg_oracle as O
+from tests.gpu_util import assert_close_attn, bf16_ulp, host64, note
+from workloads import WORKLOADS, expected_planted_kinds, make_qkv, norm_weights, sample_queries
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _layer(gpu, wl, layer=0):
+    g = wl.geom
+    q, k, v = make_qkv(wl, device=DEV, layer=layer)
+    idx = sample_queries(g.S, wl.n_q, wl.idx_seed + layer)
+    norm = None
+    if wl.norm_rope:
+        wq, wk = norm_weights(g.D, wl.seed)
+        norm = (torch.from_numpy(wq).to(DEV), torch.from_numpy(wk).to(DEV), wl.eps, wl.rope_base)
+    o, kind, mse, qn, kn = gpu.sparse_layer(q, k, v, torch.from_numpy(idx).to(DEV), g.F, g.HH, g.WW, wl.w_f, wl.w_p,
+                                            norm=norm)
+    torch.cuda.synchronize()
+    return q, k, v, idx, norm, o, kind.cpu().numpy(), mse.cpu().numpy(), qn, kn
+
+
+def _check_layer(gpu, wl, rows_per_head, heads=None, layer=0, planted_expected=True):
+    g = wl.geom
+    q, k, v, idx, norm, o, kind, mse, qn, kn = _layer(gpu, wl, layer)
+    sc = O.default_scale(g.D)
+    heads = range(g.H) if heads is None else heads
+    rng = np.random.default_rng(99 + layer)
+    if norm is not None:
+        wq, wk = norm_weights(g.D, wl.seed)
+        for h in list(heads)[:2]:
+            for src, w, out in ((q, wq, qn), (k, wk, kn)):
+                want = O.rope_3d(O.rms_norm(host64(src[0, h]), w.astype(np.float64), wl.eps), g.F, g.HH, g.WW,
+                                 wl.rope_base)
+                pair = np.repeat(np.hypot(want[:, 0::2], want[:, 1::2]), 2, axis=1)
+                assert (np.abs(host64(out[0, h]) - want) <= bf16_ulp(want) + 1e-6 + 2.0 ** -20 * pair).all()
+    # profiling on what the GPU profiled
+    for h in heads:
+        qh, kh, vh = host64(qn[0, h]), host64(kn[0, h]), host64(v[0, h])
+        a, c, kd = O.profile_head(qh, kh, vh, idx, g.F, g.P, wl.w_f, wl.w_p, sc)
+        assert O.choices_agree(np.array([kind[0, h]]), np.array([kd]), np.array([[a, c]]), 1e-6).all(), \
+            (h, kind[0, h], kd, a, c, mse[0, h])
+        # sparse attention output under the chosen kind, rows sampled plus both ends
+        rows = np.unique(np.concatenate([rng.choice(g.S, rows_per_head, replace=False), np.arange(0, 64),
+                                         np.arange(g.S - 64, g.S)]))
+        want = O.head_attention_rows(qh, kh, vh, rows, int(kind[0, h]), g.F, g.P, wl.w_f, wl.w_p, sc)
+        assert_close_attn(host64(o[0, h])[rows], want, f"{wl.name} head {h} kind {kind[0, h]}")
+    exp = expected_planted_kinds(wl, layer)
+    if exp is not None and planted_expected:
+        assert np.array_equal(kind[0], exp), (kind[0], exp)
+
+
+def test_step_720p_subgrid_4_frames(gpu):
+    wl = WORKLOADS["hunyuan720p_f4"]
+    note(f"full layer {wl.name} {wl.geom}")
+    # With only 4 frames the +-1 frame spatial window already holds 5/8 of all keys, so the
+    # spatial mask wins for temporal-planted heads too; only agreement with the oracle counts.
+    _check_layer(gpu, wl, rows_per_head=192, planted_expected=False)
+
+
+def test_step_720p_full_grid(gpu):
+    wl = WORKLOADS["hunyuan720p"]
+    note(f"full layer {wl.name} {wl.geom}")
+    _check_layer(gpu, wl, rows_per_head=24, heads=range(0, wl.geom.H, 3))
+
+
+def test_step_wan_shape_with_norm(gpu):
+    wl = WORKLOADS["wan"]
+    note(f"full layer {wl.name} {wl.geom}")
+    _check_layer(gpu, wl, rows_per_head=32, heads=range(0, wl.geom.H, 5))
