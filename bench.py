@@ -39,7 +39,21 @@ def parse():
     ap.add_argument("--steps", type=int, default=12)
     ap.add_argument("--warmup", type=int, default=4)
     ap.add_argument("--layers", type=int, default=4)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 3 times (the reference kernel that scales "
+                         "the FETCH_SIZE / WRITE_SIZE counters to bytes) and exit")
     return ap.parse_args()
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "repeats": 3}), flush=True)
 
 
 def tile_flops(svg, kind, g, w_f, w_p, bm, bn):
@@ -85,7 +99,7 @@ def measured_traffic():
 
 
 def cpu_baseline(q, k, v, kinds, g, w_f, w_p):
-    """The fp64 oracle on a bounded sample of the same layer: 512 query rows of one spatial
+    """The fp64 oracle on a bounded sample of the same layer: 6144 query rows of one spatial
     and one temporal head against all 118800 keys; token-level FLOPs / wall time."""
     import numpy as np
     import oracle.svg_oracle as O
@@ -96,7 +110,7 @@ def cpu_baseline(q, k, v, kinds, g, w_f, w_p):
         threads = len(os.sched_getaffinity(0))
     heads = [int(np.argmax(kinds == 0)), int(np.argmax(kinds == 1))]
     rng = np.random.default_rng(123)
-    rows = np.sort(rng.choice(g.S, 512, replace=False))
+    rows = np.sort(rng.choice(g.S, 6144, replace=False))
     sc = 1.0 / math.sqrt(g.D)
     flops = 0.0
     elapsed = 0.0
@@ -110,13 +124,16 @@ def cpu_baseline(q, k, v, kinds, g, w_f, w_p):
         m = O.mask_rows(kind, rows, g.S, g.P, w_f, w_p)
         flops += 4.0 * g.D * float(m.sum())
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": "fp64 numpy oracle, sparse attention of 512 sampled query rows of one spatial and one "
+            "sample": "fp64 numpy oracle, sparse attention of 6144 sampled query rows of one spatial and one "
                       "temporal head of the 720p layer (S=118800, D=128) against all keys; token-level FLOPs",
             "seconds": round(elapsed, 2)}
 
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards over heads with no "
               f"exchange, so per-GPU throughput is the one-GPU figure.", file=sys.stderr)

@@ -72,7 +72,8 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 size_t profile_ws_bytes(const svg_geom& g, int32_t n_q) {
   const int32_t S = g.F * g.HH * g.WW;
   svg::ProfilePlan p = svg::profile_plan(g.B * g.H, S, g.D, n_q);
-  return align_up(p.ml_floats * sizeof(float), 256) + align_up(p.o_floats * sizeof(float), 256);
+  return align_up(p.ml_floats * sizeof(float), 256) + align_up(p.o_floats * sizeof(float), 256) +
+         align_up(p.sq_doubles * sizeof(double), 256);
 }
 
 size_t attn_ws_bytes(const svg_geom& g) { return align_up((size_t)g.B * g.H * sizeof(int32_t), 256); }
@@ -157,6 +158,7 @@ SVG_API svg_status svg_profile_heads(const void* q, const void* k, const void* v
   a.keys_per_split = plan.keys_per_split;
   a.part_ml = (float*)ws;
   a.part_o = (float*)((char*)ws + align_up(plan.ml_floats * sizeof(float), 256));
+  a.row_sq = (double*)((char*)a.part_o + align_up(plan.o_floats * sizeof(float), 256));
   a.mse = mse_out;
   a.kind = kind_out;
   return hip_status(svg::launch_profile(a, (hipStream_t)stream), "svg_profile_heads");

@@ -9,16 +9,19 @@
 // first row's lower end and the last row's upper end; only boundary tiles need the
 // per-element mask.
 //
-// Work decomposition: one workgroup (4 wavefronts of 64) per (head, 128-row query block);
-// wavefront w owns query rows 32w..32w+31 of the block.  Key/value tiles of 64 rows are
-// staged in LDS (double-buffered: the next tile's global loads are in flight while the
-// current one is consumed) and shared by the four wavefronts.
+// Work decomposition: one workgroup of 8 wavefronts per (head, 256-row query block), two
+// groups of 4 wavefronts with 128 rows each (32 rows per wavefront), scheduled in ping-pong
+// (see "Ping-pong schedule" below).  Key/value tiles of 64 rows are double-buffered in LDS and
+// shared by all 8 wavefronts.  They are copied from HBM straight into LDS
+// (global_load_lds_dwordx4: no register staging); each wavefront instruction fills 1 KB of
+// LDS, and the 16-byte chunks of a row are XOR-swizzled by row on the global side so that
+// both LDS read patterns below are free of bank conflicts.
 //
 // Per tile and wavefront, with v_mfma_f32_32x32x16_bf16 (lane l: row/col l%32, k-half l/32):
 //   S^T[key][query] = K Q^T      A = K rows from LDS (one 16-byte read per MFMA),
 //                                B = Q kept in registers for the whole loop.
 //   The accumulator puts one query per lane (column l%32) and 16 keys per lane, so the row
-//   max needs one cross-half exchange and the row sum none until the end.
+//   max needs one cross-half exchange (v_permlane32_swap) and the row sum none until the end.
 //   O^T[d][query] += V^T P^T     A = V^T read from the row-major V tile with the LDS
 //                                transpose read (ds_read_b64_tr_b16), B = P^T converted to
 //                                bf16 straight from the S^T accumulator registers: the key
@@ -35,15 +38,48 @@ namespace svg {
 
 namespace {
 
-constexpr int BM = ATTN_BM;       // query rows per workgroup
 constexpr int BN = ATTN_BN;       // keys per tile
-constexpr int NT = 256;           // threads per workgroup
 constexpr float RESCALE_SLACK = 8.0f;
 
+// Workgroups are handed to the 8 XCDs round-robin by index, and each XCD has its own L2.
+// Consecutive query blocks of a head read (almost) the same key/value tiles in the same
+// order, so each XCD is given runs of XCD_RUN consecutive work items -- about as many as it
+// keeps resident -- instead of every 8th item.
+#ifndef SVG_ATTN_XCD_RUN
+#define SVG_ATTN_XCD_RUN 32
+#endif
+// LDS operand reads are kept this many MFMAs ahead of their use in the QK^T and PV phases
+// (the LDS read latency exceeds two back-to-back MFMAs).  0 leaves the order to the compiler.
+#ifndef SVG_ATTN_QK_AHEAD
+#define SVG_ATTN_QK_AHEAD 4
+#endif
+#ifndef SVG_ATTN_PV_AHEAD
+#define SVG_ATTN_PV_AHEAD 2
+#endif
+constexpr int NXCD = 8;
+constexpr int XCD_RUN = SVG_ATTN_XCD_RUN;
+
+// Bijection on [0, n): block b runs on XCD b % 8; XCD x takes runs x, x+8, x+16, ... of
+// XCD_RUN consecutive items.  A tail of fewer than 8 runs keeps the identity order.
+__device__ __forceinline__ int32_t xcd_item(int32_t b, int32_t n) {
+  const int32_t full = (n / (NXCD * XCD_RUN)) * (NXCD * XCD_RUN);
+  if (b >= full) return b;
+  const int32_t x = b % NXCD, slot = b / NXCD;
+  return (x + NXCD * (slot / XCD_RUN)) * XCD_RUN + slot % XCD_RUN;
+}
+
+// Tile geometry in LDS: rows of D bf16 (no padding), 16-byte chunks XOR-swizzled per row.
 template <int D>
-struct Lds {
-  static constexpr int KS = D + 8;    // K row stride (elements): 16-byte skew per row
-  static constexpr int VS = D + 32;   // V row stride (elements): 64-byte skew per row
+struct TileLds {
+  static constexpr int CPR = D / 8;            // 16-byte chunks per row
+  static constexpr int RPB = 16 / CPR;         // rows per 256-byte bank period
+  static constexpr int ROW_BYTES = D * 2;
+  static constexpr int TILE_BYTES = BN * ROW_BYTES;
+  // K is read 16 rows x one chunk per 16 lanes: spread those rows over all 16 chunk slots.
+  static __device__ __forceinline__ int swz_k(int r) { return (r / RPB) & (CPR - 1); }
+  // V is read by the transpose read, 4 rows x 4 consecutive chunks per 32 lanes: give each
+  // of the 4 rows its own group of 4 chunk slots.
+  static __device__ __forceinline__ int swz_v(int r) { return 4 * ((r / RPB) & (CPR / 4 - 1)); }
 };
 
 __global__ void head_order_kernel(const uint8_t* __restrict__ kind, int32_t* __restrict__ order, int32_t BH) {
@@ -56,17 +92,204 @@ __global__ void head_order_kernel(const uint8_t* __restrict__ kind, int32_t* __r
     if (kind[h] == KIND_TEMPORAL) order[n++] = h;
 }
 
-template <int D>
-__global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnArgs a, int32_t nqb) {
-  constexpr int KS = Lds<D>::KS;
-  constexpr int VS = Lds<D>::VS;
-  constexpr int NDB = D / 32;                // 32-wide d blocks of the output
-  constexpr int NKS = D / 16;                // k-steps of the QK^T product
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2][BN * KS];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[2][BN * VS];
+// ------------------------------------------------------------------------------------------
+// Ping-pong schedule.  A workgroup of 8 wavefronts owns 256 query rows: group A (wavefronts
+// 0-3) rows 0-127 and group B (wavefronts 4-7) rows 128-255, 32 rows per wavefront; the two
+// wavefronts that share a SIMD belong to different groups.  Both groups walk the same key
+// tiles t_0..t_{T-1} (the union of their ranges; a group skips the tiles outside its own
+// range) in phases separated by workgroup barriers:
+//   M(i) : O^T += V^T P^T for tile i-1, then S^T = K Q^T for tile i     (matrix cores)
+//   X(i) : mask, online softmax and bf16 packing of P for tile i        (vector ALUs)
+// Group A runs M(0) X(0) M(1) X(1) ... M(T); group B runs the same sequence one phase later,
+// so in every phase one group feeds the matrix cores while the other does exponentials.
+// Group A issues the HBM -> LDS copies at the end of each of its M phases, once its own LDS
+// reads are done: after M(j), K(t_{j+1}) and V(t_j); it waits for them at the end of X(j), and
+// the next barrier publishes them.  Every M phase starts with an explicit wait on vector
+// memory (free at run time -- no copy of that wavefront is in flight then) so that the
+// compiler knows no copy is pending and can count the LDS waits instead of draining them.
+// K and V are double-buffered in four distinct LDS objects, and the phase loop is unrolled by
+// four so every access names one of them (the compiler then knows the copies in flight do
+// not alias the reads).
+// ------------------------------------------------------------------------------------------
+constexpr int PP_BM = 256;        // query rows per workgroup
+constexpr int PP_NT = 512;        // 8 wavefronts
 
-  const int32_t rank = blockIdx.x / nqb;
-  const int32_t qb = blockIdx.x - rank * nqb;
+// Per-lane state of one query row (lane's query = column l%32 of its wavefront's 32 rows).
+template <int D>
+struct RowState {
+  f32x16 oacc[D / 32];       // O^T accumulator, one 32-row d block per entry
+  f32x16 sacc[2];            // S^T of the current tile (two 32-key blocks)
+  bf16x8 pb[BN / 16];        // P^T of the previous tile as bf16 MFMA operands (16 keys each)
+  float m_ref;               // reference max (log2 units) of oacc / l_run
+  float l_run;               // this lane's share of the row sum
+};
+
+// the value of x held by lane l^32
+__device__ __forceinline__ float other_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  // lanes 0-31 find their partner in r[1], lanes 32-63 in r[0]; the other entry is x itself
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]) - x;
+}
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(fmaxf(x, __uint_as_float(r[0])), __uint_as_float(r[1]));
+}
+
+// S^T = K Q^T for the 64 keys of a tile: two independent 32-key accumulation chains.
+template <int D>
+__device__ __forceinline__ void phase_qk(RowState<D>& st, const bf16x8 (&qf)[D / 16], const char* kb, int l32,
+                                         int hh) {
+  using T = TileLds<D>;
+  constexpr int NKS = D / 16;
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st.sacc[blk][r] = 0.f;
+#pragma unroll
+  for (int s = 0; s < NKS; ++s)
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const int r = blk * 32 + l32;
+      const bf16x8 ak = *reinterpret_cast<const bf16x8*>(kb + r * T::ROW_BYTES + 16 * ((2 * s + hh) ^ T::swz_k(r)));
+      st.sacc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[s], st.sacc[blk], 0, 0, 0);
+    }
+  if constexpr (SVG_ATTN_QK_AHEAD > 0) {
+    constexpr int AH = SVG_ATTN_QK_AHEAD;           // one 16-byte read per MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, AH, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * NKS - AH; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, AH, 0);
+  }
+}
+
+// O^T += V^T P^T for the 64 keys of a tile (four 16-key steps).
+template <int D>
+__device__ __forceinline__ void phase_pv(RowState<D>& st, const char* vbase, int v_row, int v_col) {
+  using T = TileLds<D>;
+  constexpr int NDB = D / 32;
+#pragma unroll
+  for (int s = 0; s < BN / 16; ++s) {
+    const int r0 = 16 * s + v_row;          // rows of the two transpose reads: r0, r0 + 8
+    const char* v0 = vbase + r0 * T::ROW_BYTES;
+    const char* v1 = v0 + 8 * T::ROW_BYTES;
+    const int sw0 = T::swz_v(r0), sw1 = T::swz_v(r0 + 8);
+#pragma unroll
+    for (int j = 0; j < NDB; ++j) {
+      const int col = 32 * j + v_col;       // logical element column
+      const int cb = 2 * (col & 7);         // byte inside the 16-byte chunk
+      const i16x4 lo = lds_read_tr(reinterpret_cast<const bf16*>(v0 + 16 * ((col >> 3) ^ sw0) + cb));
+      const i16x4 hi = lds_read_tr(reinterpret_cast<const bf16*>(v1 + 16 * ((col >> 3) ^ sw1) + cb));
+      const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      st.oacc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, st.pb[s], st.oacc[j], 0, 0, 0);
+    }
+  }
+  if constexpr (SVG_ATTN_PV_AHEAD > 0) {
+    constexpr int AH = SVG_ATTN_PV_AHEAD;           // two transpose reads per MFMA
+    constexpr int NM = (BN / 16) * NDB;
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * AH, 0);
+#pragma unroll
+    for (int i = 0; i < NM - AH; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, AH, 0);
+  }
+}
+
+// Exact token mask (boundary tiles), online softmax with lazy rescaling, bf16 P^T operands.
+template <int D>
+__device__ __forceinline__ void phase_softmax(RowState<D>& st, int32_t k0, bool edge, int32_t my_lo, int32_t my_hi,
+                                              float c, int hh) {
+  constexpr int NDB = D / 32;
+  if (edge) {
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int32_t key = k0 + blk * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+        st.sacc[blk][r] = (key < my_lo || key >= my_hi) ? -INFINITY : st.sacc[blk][r];
+      }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st.sacc[blk][r]);
+  mx = max_halves(mx) * c;
+  const bool bump = mx > st.m_ref + RESCALE_SLACK;
+  if (__any(bump)) {
+    const float m_new = bump ? mx : st.m_ref;
+    const float alpha = (st.m_ref == -INFINITY) ? 0.f : exp2f(st.m_ref - m_new);
+    st.l_run *= alpha;
+#pragma unroll
+    for (int j = 0; j < NDB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.oacc[j][r] *= alpha;
+    st.m_ref = m_new;
+  }
+  const float m_use = (st.m_ref == -INFINITY) ? 0.f : st.m_ref;
+  float rsum = 0.f;
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(st.sacc[blk][r], c, -m_use));
+      st.sacc[blk][r] = p;
+      rsum += p;
+    }
+  st.l_run += rsum;
+#pragma unroll
+  for (int s = 0; s < BN / 16; ++s)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) st.pb[s][e] = (bf16)st.sacc[s >> 1][8 * (s & 1) + e];
+}
+
+// Workgroup barrier without a memory fence.  The only data one wavefront hands another
+// through LDS here are the copied tiles, whose completion the issuing wavefronts wait for
+// explicitly (vmcnt) before the barrier that publishes them; every LDS read is consumed by
+// its own wavefront before that wavefront reaches the next barrier.  A fenced barrier would
+// also wait for the copies just issued for the phase after next.  The empty asm statements
+// keep the compiler from moving LDS accesses across the barrier.
+__device__ __forceinline__ void phase_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Copy of one K or V tile into LDS by the four wavefronts of one group (wb = 0..3).
+template <int D>
+__device__ __forceinline__ void pp_load(const bf16* __restrict__ src, int32_t k0, int32_t S, bf16* dst, int wb,
+                                        int lane, bool is_v) {
+  using T = TileLds<D>;
+  constexpr int PER_WAVE = T::TILE_BYTES / 1024 / 4;
+#pragma unroll
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int kb = (wb * PER_WAVE + i) * 1024;
+    const int o = kb + 16 * lane;
+    const int row = o / T::ROW_BYTES;
+    const int pc = (o % T::ROW_BYTES) / 16;
+    const int lc = pc ^ (is_v ? T::swz_v(row) : T::swz_k(row));
+    const size_t grow = (size_t)min(k0 + row, S - 1);
+    __builtin_amdgcn_global_load_lds(src + grow * D + 8 * lc,
+                                     (__attribute__((address_space(3))) void*)((char*)dst + kb), 16, 0, 0);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(PP_NT, 1) void attn_fwd_kernel(AttnArgs a, int32_t nqb) {
+  constexpr int NDB = D / 32;
+  constexpr int NKS = D / 16;
+  __shared__ __attribute__((aligned(1024))) bf16 K0[BN * D];
+  __shared__ __attribute__((aligned(1024))) bf16 K1[BN * D];
+  __shared__ __attribute__((aligned(1024))) bf16 V0[BN * D];
+  __shared__ __attribute__((aligned(1024))) bf16 V1[BN * D];
+
+  const int32_t item = xcd_item((int32_t)blockIdx.x, (int32_t)gridDim.x);
+  const int32_t rank = item / nqb;
+  const int32_t qb = item - rank * nqb;
   const int32_t bh = a.order ? a.order[rank] : rank;
   int kind = (a.force_dense || a.kind == nullptr) ? KIND_DENSE : (int)a.kind[bh];
   if (kind != KIND_SPATIAL && kind != KIND_TEMPORAL) kind = KIND_DENSE;
@@ -86,130 +309,126 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnArgs a, int32_t nqb
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  // wavefronts w and w+4 share a SIMD, so the groups are wavefronts 0-3 and 4-7
+  const int grp = wave >> 2;                 // 0: group A, 1: group B
+  const int wig = wave & 3;                  // wavefront within its group
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
-  const int32_t q0 = qb * BM;
-  const int32_t q_last = min(q0 + BM, a.S) - 1;
-  int32_t lo_first, hi_first, lo_last, hi_last;
-  band_interval(band, q0, lo_first, hi_first);
-  band_interval(band, q_last, lo_last, hi_last);
-  const int32_t t_begin = lo_first / BN;
-  const int32_t t_end = (hi_last + BN - 1) / BN;
+  // tiles of the whole workgroup (union of both groups' ranges)
+  const int32_t q0 = qb * PP_BM;
+  const int32_t q_last = min(q0 + PP_BM, a.S) - 1;
+  int32_t lo0, hi0, lo1, hi1;
+  band_interval(band, q0, lo0, hi0);
+  band_interval(band, q_last, lo1, hi1);
+  const int32_t t_begin = lo0 / BN;
+  const int32_t T = (hi1 + BN - 1) / BN - t_begin;
 
-  const int32_t my_q = q0 + wave * 32 + l32;
+  // this group's rows and tiles
+  const int32_t g0 = q0 + grp * (PP_BM / 2);
+  const bool g_live = g0 < a.S;
+  const int32_t g1 = min(g0 + PP_BM / 2, a.S) - 1;
+  int32_t glo_first = 0, ghi_first = 0, glo_last = 0, ghi_last = 0;
+  if (g_live) {
+    band_interval(band, g0, glo_first, ghi_first);
+    band_interval(band, g1, glo_last, ghi_last);
+  }
+  const int32_t gt_begin = glo_first / BN;
+  const int32_t gt_end = g_live ? (ghi_last + BN - 1) / BN : 0;
+
+  const int32_t my_q = g0 + wig * 32 + l32;
   const int32_t my_qc = min(my_q, a.S - 1);
   int32_t my_lo, my_hi;
   band_interval(band, my_qc, my_lo, my_hi);
 
+  if (grp == 0) pp_load<D>(K, t_begin * BN, a.S, K0, wig, lane, false);
   bf16x8 qf[NKS];
 #pragma unroll
   for (int s = 0; s < NKS; ++s)
     qf[s] = *reinterpret_cast<const bf16x8*>(Q + (size_t)my_qc * D + 16 * s + 8 * hh);
 
-  TileStager<D, BN, NT> stage;
-
-  f32x16 oacc[NDB];
+  RowState<D> st;
 #pragma unroll
   for (int j = 0; j < NDB; ++j)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[j][r] = 0.f;
-  float m_ref = -INFINITY;   // reference max (log2 units) the accumulators are scaled to
-  float l_run = 0.f;         // this lane's share of the row sum, relative to m_ref
+    for (int r = 0; r < 16; ++r) st.oacc[j][r] = 0.f;
+  st.m_ref = -INFINITY;
+  st.l_run = 0.f;
   const float c = a.scale * 1.44269504088896340736f;
-
-  // transpose-read coordinates of this lane inside the V tile
   const int tg = lane >> 4;
   const int ti = lane & 15;
   const int v_row = 4 * (tg >> 1) + (ti >> 2);
   const int v_col = 16 * (tg & 1) + 4 * (ti & 3);
 
-  stage.load(K, V, t_begin * BN, a.S, tid);
-  stage.template store<KS, VS>(Ks[0], Vs[0], tid);
+  // everything loaded so far retires before the phase loop (see the note on counters above)
+  __builtin_amdgcn_s_waitcnt(ALLCNT0);
   __syncthreads();
 
-  for (int32_t t = t_begin; t < t_end; ++t) {
-    const int buf = (t - t_begin) & 1;
-    const bool has_next = t + 1 < t_end;
-    if (has_next) stage.load(K, V, (t + 1) * BN, a.S, tid);
+  // rel(i): tile t_begin+i lies in this group's range
+  auto rel = [&](int32_t i) { return i >= 0 && i < T && t_begin + i >= gt_begin && t_begin + i < gt_end; };
+  auto edge = [&](int32_t i) {
+    const int32_t k0 = (t_begin + i) * BN;
+    return !(k0 >= glo_last && k0 + BN <= ghi_first);
+  };
+  // M(i) with the buffers of its parity: PV(i-1) reads vprev, QK(i) reads kcur
+  auto do_m = [&](int32_t i, const bf16* vprev, const bf16* kcur) {
+    __builtin_amdgcn_s_waitcnt(VMCNT0);
+    if (rel(i - 1)) phase_pv<D>(st, reinterpret_cast<const char*>(vprev), v_row, v_col);
+    if (rel(i)) phase_qk<D>(st, qf, reinterpret_cast<const char*>(kcur), l32, hh);
+  };
+  auto do_x = [&](int32_t i) {
+    if (rel(i)) phase_softmax<D>(st, (t_begin + i) * BN, edge(i), my_lo, my_hi, c, hh);
+  };
+  // group A's copies after M(j): K(t_{j+1}) -> kdst, V(t_j) -> vdst
+  auto do_load = [&](int32_t j, bf16* kdst, bf16* vdst) {
+    if (j + 1 < T) pp_load<D>(K, (t_begin + j + 1) * BN, a.S, kdst, wig, lane, false);
+    if (j < T) pp_load<D>(V, (t_begin + j) * BN, a.S, vdst, wig, lane, true);
+  };
 
-    // ---- S^T = K Q^T for keys [k0, k0+64) (two 32-key blocks) ----
-    f32x16 sacc[2];
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[blk][r] = 0.f;
-#pragma unroll
-      for (int s = 0; s < NKS; ++s) {
-        const bf16x8 ak = *reinterpret_cast<const bf16x8*>(&Ks[buf][(blk * 32 + l32) * KS + 16 * s + 8 * hh]);
-        sacc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[s], sacc[blk], 0, 0, 0);
-      }
+  const int32_t n_phase = 2 * T + 2;
+  for (int32_t m = 0;; ++m) {
+    // phase 4m: A: M(2m) [V1, K0], then copies K(t_{2m+1}) -> K1, V(t_{2m}) -> V0; B: X(2m-1)
+    if (grp == 0) {
+      do_m(2 * m, V1, K0);
+      do_load(2 * m, K1, V0);
+    } else {
+      do_x(2 * m - 1);
     }
-
-    // ---- exact token mask on boundary tiles ----
-    const int32_t k0 = t * BN;
-    if (!(k0 >= lo_last && k0 + BN <= hi_first)) {
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int32_t key = k0 + blk * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (key < my_lo || key >= my_hi) sacc[blk][r] = -INFINITY;
-        }
+    phase_barrier();
+    if (4 * m + 1 >= n_phase) break;
+    // phase 4m+1: A: X(2m), copies retire; B: M(2m) [V1, K0]
+    if (grp == 0) {
+      do_x(2 * m);
+      __builtin_amdgcn_s_waitcnt(VMCNT0);
+    } else {
+      do_m(2 * m, V1, K0);
     }
-
-    // ---- online softmax (one query per lane; the other half-wave holds the other keys) ----
-    float mx = -INFINITY;
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[blk][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
-    const bool bump = mx > m_ref + RESCALE_SLACK;
-    if (__any(bump)) {
-      const float m_new = bump ? mx : m_ref;
-      const float alpha = (m_ref == -INFINITY) ? 0.f : exp2f(m_ref - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int j = 0; j < NDB; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[j][r] *= alpha;
-      m_ref = m_new;
+    phase_barrier();
+    if (4 * m + 2 >= n_phase) break;
+    // phase 4m+2: A: M(2m+1) [V0, K1], then copies K(t_{2m+2}) -> K0, V(t_{2m+1}) -> V1; B: X(2m)
+    if (grp == 0) {
+      do_m(2 * m + 1, V0, K1);
+      do_load(2 * m + 1, K0, V1);
+    } else {
+      do_x(2 * m);
     }
-    const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-    float rsum = 0.f;
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[blk][r], c, -m_use));
-        sacc[blk][r] = p;
-        rsum += p;
-      }
-    l_run += rsum;
-
-    // ---- O^T += V^T P^T, four 16-key steps ----
-#pragma unroll
-    for (int s = 0; s < BN / 16; ++s) {
-      bf16x8 pb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pb[e] = (bf16)sacc[s >> 1][8 * (s & 1) + e];
-      const bf16* vb = &Vs[buf][(16 * s + v_row) * VS + v_col];
-#pragma unroll
-      for (int j = 0; j < NDB; ++j) {
-        const bf16x8 av = load_vt(vb + j * 32, VS);
-        oacc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb, oacc[j], 0, 0, 0);
-      }
+    phase_barrier();
+    if (4 * m + 3 >= n_phase) break;
+    // phase 4m+3: A: X(2m+1), copies retire; B: M(2m+1) [V0, K1]
+    if (grp == 0) {
+      do_x(2 * m + 1);
+      __builtin_amdgcn_s_waitcnt(VMCNT0);
+    } else {
+      do_m(2 * m + 1, V0, K1);
     }
-
-    if (has_next) stage.template store<KS, VS>(Ks[buf ^ 1], Vs[buf ^ 1], tid);
-    __syncthreads();
+    phase_barrier();
+    if (4 * m + 4 >= n_phase) break;
   }
 
   // ---- epilogue: divide by the row sum, round to bf16, store this lane's query row ----
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const float inv = 1.f / l_tot;
   if (my_q < a.S) {
+    const float l_tot = st.l_run + other_half(st.l_run);
+    const float inv = 1.f / l_tot;
     bf16* orow = O + (size_t)my_q * D;
 #pragma unroll
     for (int j = 0; j < NDB; ++j)
@@ -217,7 +436,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnArgs a, int32_t nqb
       for (int rq = 0; rq < 4; ++rq) {
         bf16x4 ov;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ov[e] = (bf16)(oacc[j][4 * rq + e] * inv);
+        for (int e = 0; e < 4; ++e) ov[e] = (bf16)(st.oacc[j][4 * rq + e] * inv);
         *reinterpret_cast<bf16x4*>(orow + 32 * j + 8 * rq + 4 * hh) = ov;
       }
   }
@@ -226,7 +445,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnArgs a, int32_t nqb
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
-  const int32_t nqb = (a.S + BM - 1) / BM;
+  const int32_t nqb = (a.S + PP_BM - 1) / PP_BM;
   if (a.order != nullptr && a.kind != nullptr && !a.force_dense) {
     head_order_kernel<<<1, 64, 0, st>>>(a.kind, a.order, a.BH);
     hipError_t e = hipGetLastError();
@@ -236,9 +455,9 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
   if (a.kind == nullptr || a.force_dense) b.order = nullptr;
   const dim3 grid((unsigned)((int64_t)nqb * a.BH));
   if (a.D == 128) {
-    attn_fwd_kernel<128><<<grid, NT, 0, st>>>(b, nqb);
+    attn_fwd_kernel<128><<<grid, PP_NT, 0, st>>>(b, nqb);
   } else if (a.D == 64) {
-    attn_fwd_kernel<64><<<grid, NT, 0, st>>>(b, nqb);
+    attn_fwd_kernel<64><<<grid, PP_NT, 0, st>>>(b, nqb);
   } else {
     return hipErrorInvalidValue;
   }

@@ -14,9 +14,11 @@
 // Keys are frame-major here: the spatial mask is a per-query interval of frames, the
 // temporal mask compares in-frame positions (key mod P).  Each wavefront writes its
 // unnormalised partial state (reference max, row sum, O) to the workspace.
-// Pass 2: one workgroup per head merges the partial states (log-sum-exp weights), forms the
-// three outputs of each sampled row, accumulates the two squared-error sums in fp64 and
-// stores mse (fp32) and the kind, deciding on the stored fp32 values (ties -> spatial).
+// Pass 2: one workgroup per (head, sampled row) merges that row's partial states with
+// log-sum-exp weights, forms its three outputs (one channel per thread) and sums the two
+// squared errors over the channels in fp64.
+// Pass 3: one workgroup per head sums the per-row errors in a fixed order, stores mse (fp32)
+// and the kind, deciding on the stored fp32 values (ties -> spatial).
 // HBM-bound: K and V of every head are read once.
 #include "svg_internal.h"
 
@@ -28,7 +30,7 @@ constexpr int NT = 512;            // partial pass
 constexpr int NT_RED = 256;        // reduce pass
 constexpr int TILE = 64;
 constexpr int QG = 64;           // sampled queries per workgroup
-constexpr int MAX_SPLIT = 32;
+constexpr int MAX_SPLIT = 128;
 constexpr int TARGET_WGS = 512;
 constexpr float RESCALE_SLACK = 8.0f;
 
@@ -155,14 +157,24 @@ __global__ __launch_bounds__(NT, 1) void profile_partial_kernel(ProfileArgs a) {
       sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, bq, sacc, 0, 0, 0);
     }
 
-    const int32_t kbase = ks + t * TILE + kp * 32;
+    const int32_t kbase = ks + t * TILE + kp * 32 + 4 * hh;
+    // in-frame position of this lane's keys: one division per tile when a frame holds at
+    // least 32 tokens (a lane's keys then cross at most one frame boundary)
+    const int32_t pbase = (int32_t)fmod_((uint32_t)kbase, a.divP);
     float pd[16], psp[16], ptp[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int32_t key = kbase + 8 * (r >> 2) + 4 * hh + (r & 3);
+      const int32_t dk = 8 * (r >> 2) + (r & 3);
+      const int32_t key = kbase + dk;
       const float s2 = sacc[r] * c;
       const bool valid = key < ke;
-      const int32_t pk = (int32_t)fmod_((uint32_t)min(key, a.S - 1), a.divP);
+      int32_t pk;
+      if (a.P >= 32) {
+        pk = pbase + dk;
+        pk -= (pk >= a.P) ? a.P : 0;
+      } else {
+        pk = (int32_t)fmod_((uint32_t)key, a.divP);
+      }
       const int32_t dp = pk - pq;
       pd[r] = valid ? s2 : -INFINITY;
       psp[r] = (valid && key >= sp_lo && key < sp_hi) ? s2 : -INFINITY;
@@ -221,56 +233,70 @@ __global__ __launch_bounds__(NT, 1) void profile_partial_kernel(ProfileArgs a) {
 }
 
 template <int D>
-__global__ __launch_bounds__(NT_RED) void profile_reduce_kernel(ProfileArgs a) {
-  __shared__ float wts[3][QG][2 * MAX_SPLIT];   // merge weight of each partial state
-  __shared__ double red[2][NT_RED];
-  const int32_t bh = blockIdx.x;
+__global__ __launch_bounds__(D) void profile_merge_kernel(ProfileArgs a) {
+  __shared__ float sm[3][2 * MAX_SPLIT], sl[3][2 * MAX_SPLIT], wt[3][2 * MAX_SPLIT];
+  __shared__ double red[2][D];
+  const int32_t bh = blockIdx.x / a.n_q;
+  const int32_t qg = blockIdx.x - bh * a.n_q;
   const int tid = threadIdx.x;
   const int32_t nparts = 2 * a.nsplit;
   const int32_t qpad = a.n_zq * QG;
-  double acc_sp = 0.0, acc_tp = 0.0;
-
-  for (int32_t zq = 0; zq < a.n_zq; ++zq) {
-    __syncthreads();
-    for (int item = tid; item < 3 * QG; item += NT_RED) {
-      const int x = item / QG, ql = item % QG;
-      const int32_t qg = zq * QG + ql;
-      float M = -INFINITY;
-      for (int32_t p = 0; p < nparts; ++p) {
-        const size_t slot = (((size_t)bh * nparts + p) * 3 + x) * qpad + qg;
-        M = fmaxf(M, a.part_ml[slot * 2]);
-      }
-      float L = 0.f;
-      for (int32_t p = 0; p < nparts; ++p) {
-        const size_t slot = (((size_t)bh * nparts + p) * 3 + x) * qpad + qg;
-        const float m = a.part_ml[slot * 2];
-        const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
-        wts[x][ql][p] = w;
-        L += w * a.part_ml[slot * 2 + 1];
-      }
-      const float inv = (L > 0.f) ? 1.f / L : 0.f;
-      for (int32_t p = 0; p < nparts; ++p) wts[x][ql][p] *= inv;
+  for (int t = tid; t < 3 * nparts; t += D) {
+    const int x = t / nparts, p = t - (t / nparts) * nparts;
+    const size_t slot = (((size_t)bh * nparts + p) * 3 + x) * qpad + qg;
+    sm[x][p] = a.part_ml[slot * 2];
+    sl[x][p] = a.part_ml[slot * 2 + 1];
+  }
+  __syncthreads();
+  if (tid < 3) {
+    float M = -INFINITY;
+    for (int32_t p = 0; p < nparts; ++p) M = fmaxf(M, sm[tid][p]);
+    float L = 0.f;
+    for (int32_t p = 0; p < nparts; ++p) {
+      const float w = (sm[tid][p] == -INFINITY) ? 0.f : exp2f(sm[tid][p] - M);
+      wt[tid][p] = w;
+      L += w * sl[tid][p];
     }
-    __syncthreads();
-    const int32_t nq_here = min(QG, a.n_q - zq * QG);
-    for (int e = tid; e < nq_here * D; e += NT_RED) {
-      const int ql = e / D, d = e % D;
-      const int32_t qg = zq * QG + ql;
-      float o3[3];
+    const float inv = (L > 0.f) ? 1.f / L : 0.f;
+    for (int32_t p = 0; p < nparts; ++p) wt[tid][p] *= inv;
+  }
+  __syncthreads();
+  float o3[3];
 #pragma unroll
-      for (int x = 0; x < 3; ++x) {
-        float s = 0.f;
-        for (int32_t p = 0; p < nparts; ++p) {
-          const size_t slot = (((size_t)bh * nparts + p) * 3 + x) * qpad + qg;
-          s = fmaf(wts[x][ql][p], a.part_o[slot * D + d], s);
-        }
-        o3[x] = s;
-      }
-      const double dsp = (double)o3[1] - (double)o3[0];
-      const double dtp = (double)o3[2] - (double)o3[0];
-      acc_sp += dsp * dsp;
-      acc_tp += dtp * dtp;
+  for (int x = 0; x < 3; ++x) {
+    float s = 0.f;
+    for (int32_t p = 0; p < nparts; ++p) {
+      const size_t slot = (((size_t)bh * nparts + p) * 3 + x) * qpad + qg;
+      s = fmaf(wt[x][p], a.part_o[slot * D + tid], s);
     }
+    o3[x] = s;
+  }
+  const double dsp = (double)o3[1] - (double)o3[0];
+  const double dtp = (double)o3[2] - (double)o3[0];
+  red[0][tid] = dsp * dsp;
+  red[1][tid] = dtp * dtp;
+  __syncthreads();
+  for (int s = D / 2; s > 0; s >>= 1) {
+    if (tid < s) {
+      red[0][tid] += red[0][tid + s];
+      red[1][tid] += red[1][tid + s];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    a.row_sq[2 * ((size_t)bh * a.n_q + qg) + 0] = red[0][0];
+    a.row_sq[2 * ((size_t)bh * a.n_q + qg) + 1] = red[1][0];
+  }
+}
+
+__global__ __launch_bounds__(NT_RED) void profile_finish_kernel(ProfileArgs a) {
+  __shared__ double red[2][NT_RED];
+  const int32_t bh = blockIdx.x;
+  const int tid = threadIdx.x;
+  double acc_sp = 0.0, acc_tp = 0.0;
+  for (int32_t q = tid; q < a.n_q; q += NT_RED) {
+    acc_sp += a.row_sq[2 * ((size_t)bh * a.n_q + q) + 0];
+    acc_tp += a.row_sq[2 * ((size_t)bh * a.n_q + q) + 1];
   }
   red[0][tid] = acc_sp;
   red[1][tid] = acc_tp;
@@ -283,7 +309,7 @@ __global__ __launch_bounds__(NT_RED) void profile_reduce_kernel(ProfileArgs a) {
     __syncthreads();
   }
   if (tid == 0) {
-    const double n = (double)a.n_q * D;
+    const double n = (double)a.n_q * a.D;
     const float msp = (float)(red[0][0] / n);
     const float mtp = (float)(red[1][0] / n);
     a.mse[2 * bh + 0] = msp;
@@ -297,7 +323,8 @@ __global__ __launch_bounds__(NT_RED) void profile_reduce_kernel(ProfileArgs a) {
 ProfilePlan profile_plan(int32_t BH, int32_t S, int32_t D, int32_t n_q) {
   ProfilePlan p;
   p.n_zq = (n_q + QG - 1) / QG;
-  int64_t want = (TARGET_WGS + (int64_t)BH * p.n_zq - 1) / ((int64_t)BH * p.n_zq);
+  // as many key splits as fit TARGET_WGS workgroups (two per CU) without a partial round
+  int64_t want = TARGET_WGS / ((int64_t)BH * p.n_zq);
   const int64_t max_tiles = (S + TILE - 1) / TILE;
   if (want > MAX_SPLIT) want = MAX_SPLIT;
   if (want > max_tiles) want = max_tiles;
@@ -308,21 +335,24 @@ ProfilePlan profile_plan(int32_t BH, int32_t S, int32_t D, int32_t n_q) {
   const size_t slots = (size_t)BH * (2 * p.nsplit) * 3 * (size_t)(p.n_zq * QG);
   p.ml_floats = slots * 2;
   p.o_floats = slots * (size_t)D;
+  p.sq_doubles = (size_t)BH * n_q * 2;
   return p;
 }
 
 hipError_t launch_profile(const ProfileArgs& a, hipStream_t st) {
   const dim3 g1((unsigned)((int64_t)a.BH * a.nsplit * a.n_zq));
-  const dim3 g2((unsigned)a.BH);
+  const dim3 g2((unsigned)((int64_t)a.BH * a.n_q));
+  const dim3 g3((unsigned)a.BH);
   if (a.D == 128) {
     profile_partial_kernel<128><<<g1, NT, 0, st>>>(a);
-    profile_reduce_kernel<128><<<g2, NT_RED, 0, st>>>(a);
+    profile_merge_kernel<128><<<g2, 128, 0, st>>>(a);
   } else if (a.D == 64) {
     profile_partial_kernel<64><<<g1, NT, 0, st>>>(a);
-    profile_reduce_kernel<64><<<g2, NT_RED, 0, st>>>(a);
+    profile_merge_kernel<64><<<g2, 64, 0, st>>>(a);
   } else {
     return hipErrorInvalidValue;
   }
+  profile_finish_kernel<<<g3, NT_RED, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -119,8 +119,10 @@ hipError_t launch_qknorm_rope(const RopeArgs& a, hipStream_t st) {
   const size_t lds = sizeof(float2) * (size_t)(a.F * (a.dt / 2) + a.HH * (a.dh / 2) + a.WW * (a.dw / 2));
   const int64_t total = (int64_t)a.BH * a.S;
   const int rpp = ROPE_THREADS / (a.D / 8);
+  // a persistent grid of two blocks per CU and tensor, so that each block builds its
+  // cos/sin tables once and then streams many rows
   int64_t blocks = (total + rpp * ROPE_UNROLL - 1) / (rpp * ROPE_UNROLL);
-  if (blocks > 2048) blocks = 2048;
+  if (blocks > 512) blocks = 512;
   const dim3 grid((unsigned)blocks, 2);
   if (a.D == 128) {
     qknorm_rope_kernel<128><<<grid, ROPE_THREADS, lds, st>>>(a);

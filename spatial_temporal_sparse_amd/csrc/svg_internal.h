@@ -15,6 +15,12 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // 16-byte move unit
 
+// s_waitcnt immediate (gfx9 encoding) that waits for every outstanding vector-memory load
+// and for nothing else: vmcnt = 0, expcnt = 7, lgkmcnt = 15.
+constexpr int VMCNT0 = 0x0F70;
+// ... and that also waits for every outstanding LDS / scalar-memory operation (lgkmcnt = 0).
+constexpr int ALLCNT0 = 0x0070;
+
 constexpr int KIND_SPATIAL = 0;
 constexpr int KIND_TEMPORAL = 1;
 constexpr int KIND_DENSE = 2;
@@ -175,6 +181,7 @@ struct ProfileArgs {
   int32_t nsplit, keys_per_split;
   float* part_ml;             // [BH][2*nsplit][3][n_zq*64][2]
   float* part_o;              // [BH][2*nsplit][3][n_zq*64][D]
+  double* row_sq;             // [BH][n_q][2] squared errors of each sampled row
   float* mse;                 // [BH][2]
   uint8_t* kind;              // [BH]
 };
@@ -183,7 +190,7 @@ hipError_t launch_profile(const ProfileArgs& a, hipStream_t st);
 // Split-K plan of the profiling kernel, shared by the launcher and the workspace query.
 struct ProfilePlan {
   int32_t n_zq, nsplit, keys_per_split;
-  size_t ml_floats, o_floats;
+  size_t ml_floats, o_floats, sq_doubles;
 };
 ProfilePlan profile_plan(int32_t BH, int32_t S, int32_t D, int32_t n_q);
 
