@@ -11,8 +11,8 @@
 //
 // Work decomposition: one workgroup of 8 wavefronts per (head, 256-row query block), two
 // groups of 4 wavefronts with 128 rows each (32 rows per wavefront), scheduled in ping-pong
-// (see "Ping-pong schedule" below).  Key/value tiles of 64 rows are double-buffered in LDS and
-// shared by all 8 wavefronts.  They are copied from HBM straight into LDS
+// (see "Ping-pong schedule" below).  Key tiles of 64 rows are double-buffered and value tiles
+// triple-buffered in LDS, shared by all 8 wavefronts.  They are copied from HBM straight into LDS
 // (global_load_lds_dwordx4: no register staging); each wavefront instruction fills 1 KB of
 // LDS, and the 16-byte chunks of a row are XOR-swizzled by row on the global side so that
 // both LDS read patterns below are free of bank conflicts.
@@ -48,13 +48,10 @@ constexpr float RESCALE_SLACK = 8.0f;
 #ifndef SVG_ATTN_XCD_RUN
 #define SVG_ATTN_XCD_RUN 32
 #endif
-// LDS operand reads are kept this many MFMAs ahead of their use in the QK^T and PV phases
-// (the LDS read latency exceeds two back-to-back MFMAs).  0 leaves the order to the compiler.
-#ifndef SVG_ATTN_QK_AHEAD
-#define SVG_ATTN_QK_AHEAD 4
-#endif
-#ifndef SVG_ATTN_PV_AHEAD
-#define SVG_ATTN_PV_AHEAD 2
+// LDS operand reads are issued for this many MFMAs ahead of the one that consumes them (the
+// LDS read latency exceeds two back-to-back MFMAs).
+#ifndef SVG_ATTN_M_AHEAD
+#define SVG_ATTN_M_AHEAD 3
 #endif
 constexpr int NXCD = 8;
 constexpr int XCD_RUN = SVG_ATTN_XCD_RUN;
@@ -96,20 +93,25 @@ __global__ void head_order_kernel(const uint8_t* __restrict__ kind, int32_t* __r
 // Ping-pong schedule.  A workgroup of 8 wavefronts owns 256 query rows: group A (wavefronts
 // 0-3) rows 0-127 and group B (wavefronts 4-7) rows 128-255, 32 rows per wavefront; the two
 // wavefronts that share a SIMD belong to different groups.  Both groups walk the same key
-// tiles t_0..t_{T-1} (the union of their ranges; a group skips the tiles outside its own
-// range) in phases separated by workgroup barriers:
+// tiles t_0..t_{T-1} (the union of their ranges) in phases separated by workgroup barriers:
 //   M(i) : O^T += V^T P^T for tile i-1, then S^T = K Q^T for tile i     (matrix cores)
 //   X(i) : mask, online softmax and bf16 packing of P for tile i        (vector ALUs)
 // Group A runs M(0) X(0) M(1) X(1) ... M(T); group B runs the same sequence one phase later,
-// so in every phase one group feeds the matrix cores while the other does exponentials.
-// Group A issues the HBM -> LDS copies at the end of each of its M phases, once its own LDS
-// reads are done: after M(j), K(t_{j+1}) and V(t_j); it waits for them at the end of X(j), and
-// the next barrier publishes them.  Every M phase starts with an explicit wait on vector
-// memory (free at run time -- no copy of that wavefront is in flight then) so that the
-// compiler knows no copy is pending and can count the LDS waits instead of draining them.
-// K and V are double-buffered in four distinct LDS objects, and the phase loop is unrolled by
-// four so every access names one of them (the compiler then knows the copies in flight do
-// not alias the reads).
+// so in every phase one group feeds the matrix cores while the other does exponentials.  The
+// two parts of an M phase are one scheduling region, so the K reads of QK^T are already in
+// flight while the last PV products run.  The group in its M phase issues first (s_setprio):
+// its MFMAs are few and long, and the exponentials fill the issue slots between them.
+// Every phase runs the same code for every tile index: a tile outside a group's range is a
+// boundary tile whose element mask empties it (P^T = 0; running max and sum unchanged).
+// The HBM -> LDS copies are issued at the end of the M phases, once the issuing group's LDS
+// reads are done, and split between the groups: after M(j), group A copies K(t_{j+1}) (into
+// the K buffer M(j-1) read) and group B copies V(t_{j+1}) (into the V buffer of V(t_{j-2})).
+// Each group waits for its copies at the end of its next X phase and the barrier after it
+// publishes them, one phase (K) or two phases (V) before their first reader.  So no copy is
+// in flight during an M phase; each M phase still starts with an explicit wait on vector
+// memory (free at run time) so that the compiler knows it and counts the LDS waits instead
+// of draining them.  The K buffers are two distinct LDS objects and the phase loop is
+// unrolled by four, so every K access names one of them.
 // ------------------------------------------------------------------------------------------
 constexpr int PP_BM = 256;        // query rows per workgroup
 constexpr int PP_NT = 512;        // 8 wavefronts
@@ -153,16 +155,6 @@ __device__ __forceinline__ void phase_qk(RowState<D>& st, const bf16x8 (&qf)[D /
       const bf16x8 ak = *reinterpret_cast<const bf16x8*>(kb + r * T::ROW_BYTES + 16 * ((2 * s + hh) ^ T::swz_k(r)));
       st.sacc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[s], st.sacc[blk], 0, 0, 0);
     }
-  if constexpr (SVG_ATTN_QK_AHEAD > 0) {
-    constexpr int AH = SVG_ATTN_QK_AHEAD;           // one 16-byte read per MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, AH, 0);
-#pragma unroll
-    for (int i = 0; i < 2 * NKS - AH; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, AH, 0);
-  }
 }
 
 // O^T += V^T P^T for the 64 keys of a tile (four 16-key steps).
@@ -186,17 +178,30 @@ __device__ __forceinline__ void phase_pv(RowState<D>& st, const char* vbase, int
       st.oacc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, st.pb[s], st.oacc[j], 0, 0, 0);
     }
   }
-  if constexpr (SVG_ATTN_PV_AHEAD > 0) {
-    constexpr int AH = SVG_ATTN_PV_AHEAD;           // two transpose reads per MFMA
-    constexpr int NM = (BN / 16) * NDB;
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * AH, 0);
-#pragma unroll
-    for (int i = 0; i < NM - AH; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, AH, 0);
+}
+
+// Scheduling groups of an M phase that runs PV (NPV MFMAs, two transpose reads each) and then
+// QK (NQK MFMAs, one 16-byte read each) as one region: before MFMA m the reads of MFMAs up to
+// m + AHM have been issued, across the PV -> QK boundary.
+template <int NPV>
+constexpr int m_reads_upto(int m) { return m < NPV ? 2 * (m + 1) : 2 * NPV + (m + 1 - NPV); }
+template <int M_, int NPV, int NQK, int AHM, int ISSUED>
+__device__ __forceinline__ void order_m_phase() {
+  if constexpr (M_ < NPV + NQK) {
+    constexpr int last = M_ + AHM < NPV + NQK - 1 ? M_ + AHM : NPV + NQK - 1;
+    constexpr int want = m_reads_upto<NPV>(last);
+    if constexpr (want > ISSUED) __builtin_amdgcn_sched_group_barrier(0x100, want - ISSUED, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    order_m_phase<M_ + 1, NPV, NQK, AHM, (want > ISSUED ? want : ISSUED)>();
   }
+}
+// One M phase: PV of the previous tile, then QK of the current one, as one region.
+template <int D>
+__device__ __forceinline__ void phase_m(RowState<D>& st, const bf16x8 (&qf)[D / 16], const char* vbase, const char* kb,
+                                        int v_row, int v_col, int l32, int hh) {
+  phase_pv<D>(st, vbase, v_row, v_col);
+  phase_qk<D>(st, qf, kb, l32, hh);
+  order_m_phase<0, (BN / 16) * (D / 32), 2 * (D / 16), SVG_ATTN_M_AHEAD, 0>();
 }
 
 // Exact token mask (boundary tiles), online softmax with lazy rescaling, bf16 P^T operands.
@@ -259,22 +264,24 @@ __device__ __forceinline__ void phase_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Copy of one K or V tile into LDS by the four wavefronts of one group (wb = 0..3).
+// Copy of one K or V tile into LDS by the four wavefronts of one group (wb = 0..3): per
+// wavefront, PER_WAVE instructions of 1 KB each.  The address is a wavefront-uniform tile base
+// plus a 32-bit per-lane offset; rows past the sequence end repeat its last row.
 template <int D>
 __device__ __forceinline__ void pp_load(const bf16* __restrict__ src, int32_t k0, int32_t S, bf16* dst, int wb,
                                         int lane, bool is_v) {
   using T = TileLds<D>;
   constexpr int PER_WAVE = T::TILE_BYTES / 1024 / 4;
+  constexpr int RPI = 1024 / T::ROW_BYTES;                // tile rows per instruction
+  const bf16* tile = src + (size_t)k0 * D;
+  const int pc = lane % T::CPR;
 #pragma unroll
   for (int i = 0; i < PER_WAVE; ++i) {
     const int kb = (wb * PER_WAVE + i) * 1024;
-    const int o = kb + 16 * lane;
-    const int row = o / T::ROW_BYTES;
-    const int pc = (o % T::ROW_BYTES) / 16;
+    const int row = (wb * PER_WAVE + i) * RPI + lane / T::CPR;
     const int lc = pc ^ (is_v ? T::swz_v(row) : T::swz_k(row));
-    const size_t grow = (size_t)min(k0 + row, S - 1);
-    __builtin_amdgcn_global_load_lds(src + grow * D + 8 * lc,
-                                     (__attribute__((address_space(3))) void*)((char*)dst + kb), 16, 0, 0);
+    const uint32_t off = (uint32_t)(min(row, S - 1 - k0) * D + 8 * lc);
+    __builtin_amdgcn_global_load_lds(tile + off, (__attribute__((address_space(3))) void*)((char*)dst + kb), 16, 0, 0);
   }
 }
 
@@ -284,8 +291,7 @@ __global__ __launch_bounds__(PP_NT, 1) void attn_fwd_kernel(AttnArgs a, int32_t 
   constexpr int NKS = D / 16;
   __shared__ __attribute__((aligned(1024))) bf16 K0[BN * D];
   __shared__ __attribute__((aligned(1024))) bf16 K1[BN * D];
-  __shared__ __attribute__((aligned(1024))) bf16 V0[BN * D];
-  __shared__ __attribute__((aligned(1024))) bf16 V1[BN * D];
+  __shared__ __attribute__((aligned(1024))) bf16 Vb[3][BN * D];     // V(t_j) in Vb[j % 3]
 
   const int32_t item = xcd_item((int32_t)blockIdx.x, (int32_t)gridDim.x);
   const int32_t rank = item / nqb;
@@ -311,7 +317,7 @@ __global__ __launch_bounds__(PP_NT, 1) void attn_fwd_kernel(AttnArgs a, int32_t 
   const int wave = tid >> 6;
   // wavefronts w and w+4 share a SIMD, so the groups are wavefronts 0-3 and 4-7
   const int grp = wave >> 2;                 // 0: group A, 1: group B
-  const int wig = wave & 3;                  // wavefront within its group
+  const int wig = __builtin_amdgcn_readfirstlane(wave & 3);   // wavefront within its group
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
@@ -333,15 +339,15 @@ __global__ __launch_bounds__(PP_NT, 1) void attn_fwd_kernel(AttnArgs a, int32_t 
     band_interval(band, g0, glo_first, ghi_first);
     band_interval(band, g1, glo_last, ghi_last);
   }
-  const int32_t gt_begin = glo_first / BN;
-  const int32_t gt_end = g_live ? (ghi_last + BN - 1) / BN : 0;
 
   const int32_t my_q = g0 + wig * 32 + l32;
   const int32_t my_qc = min(my_q, a.S - 1);
   int32_t my_lo, my_hi;
   band_interval(band, my_qc, my_lo, my_hi);
 
+  // first tiles: K(t_0) by group A, V(t_0) by group B
   if (grp == 0) pp_load<D>(K, t_begin * BN, a.S, K0, wig, lane, false);
+  else pp_load<D>(V, t_begin * BN, a.S, Vb[0], wig, lane, true);
   bf16x8 qf[NKS];
 #pragma unroll
   for (int s = 0; s < NKS; ++s)
@@ -352,8 +358,12 @@ __global__ __launch_bounds__(PP_NT, 1) void attn_fwd_kernel(AttnArgs a, int32_t 
   for (int j = 0; j < NDB; ++j)
 #pragma unroll
     for (int r = 0; r < 16; ++r) st.oacc[j][r] = 0.f;
+#pragma unroll
+  for (int s = 0; s < BN / 16; ++s) st.pb[s] = bf16x8{};
   st.m_ref = -INFINITY;
   st.l_run = 0.f;
+  // M(0) reads V(t_{-1}) from Vb[2] with P^T = 0: zero it so that the product is exactly zero
+  for (int o = tid; o < BN * D / 8; o += PP_NT) reinterpret_cast<u32x4*>(Vb[2])[o] = u32x4{0u, 0u, 0u, 0u};
   const float c = a.scale * 1.44269504088896340736f;
   const int tg = lane >> 4;
   const int ti = lane & 15;
@@ -364,62 +374,72 @@ __global__ __launch_bounds__(PP_NT, 1) void attn_fwd_kernel(AttnArgs a, int32_t 
   __builtin_amdgcn_s_waitcnt(ALLCNT0);
   __syncthreads();
 
-  // rel(i): tile t_begin+i lies in this group's range
-  auto rel = [&](int32_t i) { return i >= 0 && i < T && t_begin + i >= gt_begin && t_begin + i < gt_end; };
+  // edge(i): tile t_begin+i needs the element mask for some row of this group -- a boundary
+  // tile, or one outside the group's range (also any tile of a group with no rows)
   auto edge = [&](int32_t i) {
     const int32_t k0 = (t_begin + i) * BN;
-    return !(k0 >= glo_last && k0 + BN <= ghi_first);
+    return !(g_live && k0 >= glo_last && k0 + BN <= ghi_first);
   };
-  // M(i) with the buffers of its parity: PV(i-1) reads vprev, QK(i) reads kcur
-  auto do_m = [&](int32_t i, const bf16* vprev, const bf16* kcur) {
+  // M(i): PV(i-1) reads vprev, QK(i) reads kcur.  M(0) adds P^T = 0 times the zeroed V buffer;
+  // the scores of the tile past the end (stale K buffer) are masked away by X(T).
+  auto do_m = [&](const bf16* vprev, const bf16* kcur) {
     __builtin_amdgcn_s_waitcnt(VMCNT0);
-    if (rel(i - 1)) phase_pv<D>(st, reinterpret_cast<const char*>(vprev), v_row, v_col);
-    if (rel(i)) phase_qk<D>(st, qf, reinterpret_cast<const char*>(kcur), l32, hh);
+    phase_m<D>(st, qf, reinterpret_cast<const char*>(vprev), reinterpret_cast<const char*>(kcur), v_row, v_col, l32,
+               hh);
   };
   auto do_x = [&](int32_t i) {
-    if (rel(i)) phase_softmax<D>(st, (t_begin + i) * BN, edge(i), my_lo, my_hi, c, hh);
+    __builtin_amdgcn_s_setprio(0);
+    phase_softmax<D>(st, (t_begin + i) * BN, edge(i), my_lo, my_hi, c, hh);
+    __builtin_amdgcn_s_setprio(2);
   };
-  // group A's copies after M(j): K(t_{j+1}) -> kdst, V(t_j) -> vdst
-  auto do_load = [&](int32_t j, bf16* kdst, bf16* vdst) {
+  // copies after M(j): group A K(t_{j+1}) -> kdst, group B V(t_{j+1}) -> Vb[(j+1) % 3]
+  auto copy_k = [&](int32_t j, bf16* kdst) {
     if (j + 1 < T) pp_load<D>(K, (t_begin + j + 1) * BN, a.S, kdst, wig, lane, false);
-    if (j < T) pp_load<D>(V, (t_begin + j) * BN, a.S, vdst, wig, lane, true);
   };
+  auto copy_v = [&](int32_t j) {
+    if (j + 1 < T) pp_load<D>(V, (t_begin + j + 1) * BN, a.S, Vb[(j + 1) % 3], wig, lane, true);
+  };
+  auto vbuf = [&](int32_t j) { return Vb[(j + 3) % 3]; };   // V(t_j), j >= -1
 
   const int32_t n_phase = 2 * T + 2;
   for (int32_t m = 0;; ++m) {
-    // phase 4m: A: M(2m) [V1, K0], then copies K(t_{2m+1}) -> K1, V(t_{2m}) -> V0; B: X(2m-1)
+    // phase 4m: A: M(2m) [V(2m-1), K0], copies K(t_{2m+1}) -> K1; B: X(2m-1), its copies retire
     if (grp == 0) {
-      do_m(2 * m, V1, K0);
-      do_load(2 * m, K1, V0);
+      do_m(vbuf(2 * m - 1), K0);
+      copy_k(2 * m, K1);
     } else {
       do_x(2 * m - 1);
+      __builtin_amdgcn_s_waitcnt(VMCNT0);
     }
     phase_barrier();
     if (4 * m + 1 >= n_phase) break;
-    // phase 4m+1: A: X(2m), copies retire; B: M(2m) [V1, K0]
+    // phase 4m+1: A: X(2m), its copies retire; B: M(2m) [V(2m-1), K0], copies V(t_{2m+1})
     if (grp == 0) {
       do_x(2 * m);
       __builtin_amdgcn_s_waitcnt(VMCNT0);
     } else {
-      do_m(2 * m, V1, K0);
+      do_m(vbuf(2 * m - 1), K0);
+      copy_v(2 * m);
     }
     phase_barrier();
     if (4 * m + 2 >= n_phase) break;
-    // phase 4m+2: A: M(2m+1) [V0, K1], then copies K(t_{2m+2}) -> K0, V(t_{2m+1}) -> V1; B: X(2m)
+    // phase 4m+2: A: M(2m+1) [V(2m), K1], copies K(t_{2m+2}) -> K0; B: X(2m), its copies retire
     if (grp == 0) {
-      do_m(2 * m + 1, V0, K1);
-      do_load(2 * m + 1, K0, V1);
+      do_m(vbuf(2 * m), K1);
+      copy_k(2 * m + 1, K0);
     } else {
       do_x(2 * m);
+      __builtin_amdgcn_s_waitcnt(VMCNT0);
     }
     phase_barrier();
     if (4 * m + 3 >= n_phase) break;
-    // phase 4m+3: A: X(2m+1), copies retire; B: M(2m+1) [V0, K1]
+    // phase 4m+3: A: X(2m+1), its copies retire; B: M(2m+1) [V(2m), K1], copies V(t_{2m+2})
     if (grp == 0) {
       do_x(2 * m + 1);
       __builtin_amdgcn_s_waitcnt(VMCNT0);
     } else {
-      do_m(2 * m + 1, V0, K1);
+      do_m(vbuf(2 * m), K1);
+      copy_v(2 * m + 1);
     }
     phase_barrier();
     if (4 * m + 4 >= n_phase) break;
