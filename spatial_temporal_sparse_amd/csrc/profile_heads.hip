@@ -9,8 +9,12 @@
 // Its eight wavefronts cover the two 32-query halves x the two 32-key halves of each 64-key
 // tile x the two halves of the head dim (for the outputs; the scores are shared work).  Per
 // tile, S^T = K Q^T on MFMA (as in the attention kernel), then three online softmax states
-// -- dense, spatial, temporal -- each with its own running max, row sum and O^T
-// accumulator; the three PV products share the V^T operands read once from LDS.
+// -- dense, spatial, temporal -- each with its own row sum and O^T accumulator; the three PV
+// products share the V^T operands read once from LDS.  The three states share one running
+// reference max, the unmasked one: softmax does not depend on the reference, so each masked
+// state only selects the unmasked exponentials of its keys.  This is exact up to rounding
+// while a row's masked scores stay within 126 (log2 units) of its unmasked maximum; beyond
+// that the masked exponentials underflow.
 // Keys are frame-major here: the spatial mask is a per-query interval of frames, the
 // temporal mask compares in-frame positions (key mod P).  Each wavefront writes its
 // unnormalised partial state (reference max, row sum, O) to the workspace.
@@ -40,43 +44,16 @@ struct PLds {
   static constexpr int VS = D + 32;
 };
 
+// Row sum and unnormalised O^T of one softmax state (its reference max is shared).
 template <int NDB>
 struct SoftmaxState {
-  float m_ref;
   float l;
   f32x16 o[NDB];
 };
 
-// Folds one 32-key tile (scores s2 already in log2 units, -inf where masked) into a state;
-// returns p (fp32) in place of the scores.
-template <int NDB>
-__device__ __forceinline__ void state_update(SoftmaxState<NDB>& st, float (&p)[16]) {
-  float mx = -INFINITY;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, p[r]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-  const bool bump = mx > st.m_ref + RESCALE_SLACK;
-  if (__any(bump)) {
-    const float m_new = bump ? mx : st.m_ref;
-    const float alpha = (st.m_ref == -INFINITY) ? 0.f : exp2f(st.m_ref - m_new);
-    st.l *= alpha;
-#pragma unroll
-    for (int j = 0; j < NDB; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st.o[j][r] *= alpha;
-    st.m_ref = m_new;
-  }
-  const float m_use = (st.m_ref == -INFINITY) ? 0.f : st.m_ref;
-  float rs = 0.f;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    p[r] = __builtin_amdgcn_exp2f(p[r] - m_use);
-    rs += p[r];
-  }
-  st.l += rs;
-}
-
-template <int D>
+// PBIG: a frame holds at least 32 tokens, so a lane's keys (a span of 28) cross at most one
+// frame boundary and their in-frame positions follow from one division per tile.
+template <int D, bool PBIG>
 __global__ __launch_bounds__(NT, 1) void profile_partial_kernel(ProfileArgs a) {
   constexpr int KS = PLds<D>::KS;
   constexpr int VS = PLds<D>::VS;
@@ -123,9 +100,9 @@ __global__ __launch_bounds__(NT, 1) void profile_partial_kernel(ProfileArgs a) {
 
   TileStager<D, TILE, NT> stage;
   SoftmaxState<NDBW> st[3];
+  float m_ref = -INFINITY;     // reference max (log2 units) shared by the three states
 #pragma unroll
   for (int x = 0; x < 3; ++x) {
-    st[x].m_ref = -INFINITY;
     st[x].l = 0.f;
 #pragma unroll
     for (int j = 0; j < NDBW; ++j)
@@ -158,31 +135,62 @@ __global__ __launch_bounds__(NT, 1) void profile_partial_kernel(ProfileArgs a) {
     }
 
     const int32_t kbase = ks + t * TILE + kp * 32 + 4 * hh;
-    // in-frame position of this lane's keys: one division per tile when a frame holds at
-    // least 32 tokens (a lane's keys then cross at most one frame boundary)
-    const int32_t pbase = (int32_t)fmod_((uint32_t)kbase, a.divP);
+    // keys past the split's end (last tile only) do not exist
+    if (ks + (t + 1) * TILE > ke) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (kbase + 8 * (r >> 2) + (r & 3) >= ke) sacc[r] = -INFINITY;
+    }
+    // shared reference max with lazy rescaling of all three states
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
+    const bool bump = mx > m_ref + RESCALE_SLACK;
+    if (__any(bump)) {
+      const float m_new = bump ? mx : m_ref;
+      const float alpha = (m_ref == -INFINITY) ? 0.f : exp2f(m_ref - m_new);
+#pragma unroll
+      for (int x = 0; x < 3; ++x) {
+        st[x].l *= alpha;
+#pragma unroll
+        for (int j = 0; j < NDBW; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) st[x].o[j][r] *= alpha;
+      }
+      m_ref = m_new;
+    }
+    const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+    // masks as unsigned range tests: spatial key - sp_lo < sp_hi - sp_lo (frame-major keys),
+    // temporal |p_key - p_query| <= w_p on in-frame positions
+    const uint32_t sp_base = (uint32_t)(kbase - sp_lo), sp_span = (uint32_t)(sp_hi - sp_lo);
+    const int32_t pbase = PBIG ? (int32_t)fmod_((uint32_t)kbase, a.divP) : 0;
+    const uint32_t tp_span = (uint32_t)(2 * a.w_p);
     float pd[16], psp[16], ptp[16];
+    float ld = 0.f, lsp = 0.f, ltp = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int32_t dk = 8 * (r >> 2) + (r & 3);
-      const int32_t key = kbase + dk;
-      const float s2 = sacc[r] * c;
-      const bool valid = key < ke;
       int32_t pk;
-      if (a.P >= 32) {
+      if constexpr (PBIG) {
         pk = pbase + dk;
         pk -= (pk >= a.P) ? a.P : 0;
       } else {
-        pk = (int32_t)fmod_((uint32_t)key, a.divP);
+        pk = (int32_t)fmod_((uint32_t)(kbase + dk), a.divP);
       }
-      const int32_t dp = pk - pq;
-      pd[r] = valid ? s2 : -INFINITY;
-      psp[r] = (valid && key >= sp_lo && key < sp_hi) ? s2 : -INFINITY;
-      ptp[r] = (valid && dp <= a.w_p && dp >= -a.w_p) ? s2 : -INFINITY;
+      const bool in_sp = sp_base + (uint32_t)dk < sp_span;
+      const bool in_tp = (uint32_t)(pk - pq + a.w_p) <= tp_span;
+      const float pr = __builtin_amdgcn_exp2f(fmaf(sacc[r], c, -m_use));
+      pd[r] = pr;
+      psp[r] = in_sp ? pr : 0.f;
+      ptp[r] = in_tp ? pr : 0.f;
+      ld += pd[r];
+      lsp += psp[r];
+      ltp += ptp[r];
     }
-    state_update<NDBW>(st[0], pd);
-    state_update<NDBW>(st[1], psp);
-    state_update<NDBW>(st[2], ptp);
+    st[0].l += ld;
+    st[1].l += lsp;
+    st[2].l += ltp;
 
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -216,7 +224,7 @@ __global__ __launch_bounds__(NT, 1) void profile_partial_kernel(ProfileArgs a) {
     const float l_tot = st[x].l + __shfl_xor(st[x].l, 32, 64);
     const size_t slot = (((size_t)bh * nparts + part) * 3 + x) * qpad + qloc;
     if (hh == 0 && dhalf == 0) {
-      a.part_ml[slot * 2 + 0] = st[x].m_ref;
+      a.part_ml[slot * 2 + 0] = m_ref;
       a.part_ml[slot * 2 + 1] = l_tot;
     }
     float* po = a.part_o + slot * D + dhalf * (D / 2);
@@ -343,11 +351,14 @@ hipError_t launch_profile(const ProfileArgs& a, hipStream_t st) {
   const dim3 g1((unsigned)((int64_t)a.BH * a.nsplit * a.n_zq));
   const dim3 g2((unsigned)((int64_t)a.BH * a.n_q));
   const dim3 g3((unsigned)a.BH);
+  const bool pbig = a.P >= 32;
   if (a.D == 128) {
-    profile_partial_kernel<128><<<g1, NT, 0, st>>>(a);
+    if (pbig) profile_partial_kernel<128, true><<<g1, NT, 0, st>>>(a);
+    else profile_partial_kernel<128, false><<<g1, NT, 0, st>>>(a);
     profile_merge_kernel<128><<<g2, 128, 0, st>>>(a);
   } else if (a.D == 64) {
-    profile_partial_kernel<64><<<g1, NT, 0, st>>>(a);
+    if (pbig) profile_partial_kernel<64, true><<<g1, NT, 0, st>>>(a);
+    else profile_partial_kernel<64, false><<<g1, NT, 0, st>>>(a);
     profile_merge_kernel<64><<<g2, 64, 0, st>>>(a);
   } else {
     return hipErrorInvalidValue;
