@@ -44,15 +44,54 @@ struct PLds {
   static constexpr int VS = D + 32;
 };
 
-// Row sum and unnormalised O^T of one softmax state (its reference max is shared).
+// Unnormalised O^T of one softmax state (reference max and row sums are kept beside it).
 template <int NDB>
 struct SoftmaxState {
-  float l;
   f32x16 o[NDB];
 };
 
+// Scores -> P of one tile for one wavefront: the half DH of its 32 keys (16 keys, score
+// registers 8*DH .. 8*DH+7) in all three states, row sums of that half, bf16 P^T operands.
+// The reference max m_use is shared (see the header).
+template <int DH, bool PBIG>
+__device__ __forceinline__ void half_softmax(const f32x16& sacc, float c, float m_use, int32_t kbase, uint32_t sp_base,
+                                             uint32_t sp_span, int32_t pbase, int32_t pq, const ProfileArgs& a,
+                                             float (&l)[3], bf16x8 (&pb)[3]) {
+  const uint32_t tp_span = (uint32_t)(2 * a.w_p);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int r = 8 * DH + e;
+    const int32_t dk = 8 * (r >> 2) + (r & 3);
+    int32_t pk;
+    if constexpr (PBIG) {
+      pk = pbase + dk;
+      pk -= (pk >= a.P) ? a.P : 0;
+    } else {
+      pk = (int32_t)fmod_((uint32_t)(kbase + dk), a.divP);
+    }
+    const bool in_sp = sp_base + (uint32_t)dk < sp_span;
+    const bool in_tp = (uint32_t)(pk - pq + a.w_p) <= tp_span;
+    const float pr = __builtin_amdgcn_exp2f(fmaf(sacc[r], c, -m_use));
+    const float ps = in_sp ? pr : 0.f;
+    const float pt = in_tp ? pr : 0.f;
+    l[0] += pr;
+    l[1] += ps;
+    l[2] += pt;
+    pb[0][e] = (bf16)pr;
+    pb[1][e] = (bf16)ps;
+    pb[2][e] = (bf16)pt;
+  }
+}
+
 // PBIG: a frame holds at least 32 tokens, so a lane's keys (a span of 28) cross at most one
 // frame boundary and their in-frame positions follow from one division per tile.
+//
+// The two wavefronts of a (query half, key half) pair -- dhalf 0 and 1, which own the two
+// halves of the head dim of the outputs -- compute the same scores but split the softmax: each
+// turns its 16 of the 32 keys into P (three states) and hands its bf16 P^T to the other
+// through LDS.  The exchange crosses the workgroup barrier at the end of the tile, so the PV
+// products of tile t run in step t+1; V is triple-buffered for that.  Both compute the
+// (cheap) row max of all 32 keys, so they agree on every rescale.
 template <int D, bool PBIG>
 __global__ __launch_bounds__(NT, 1) void profile_partial_kernel(ProfileArgs a) {
   constexpr int KS = PLds<D>::KS;
@@ -60,8 +99,9 @@ __global__ __launch_bounds__(NT, 1) void profile_partial_kernel(ProfileArgs a) {
   constexpr int NDBW = D / 64;     // 32-wide d blocks of the output per wavefront
   constexpr int NKS = D / 16;
   __shared__ __attribute__((aligned(16))) bf16 Ks[2][TILE * KS];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[2][TILE * VS];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[3][TILE * VS];
   __shared__ __attribute__((aligned(16))) bf16 Qs[QG * KS];   // the 64 sampled rows
+  __shared__ __attribute__((aligned(16))) bf16x8 Px[2][NT / 64][3][64];   // P^T exchange
 
   int32_t bid = blockIdx.x;
   const int32_t zq = bid % a.n_zq;
@@ -69,9 +109,11 @@ __global__ __launch_bounds__(NT, 1) void profile_partial_kernel(ProfileArgs a) {
   const int32_t split = bid % a.nsplit;
   const int32_t bh = bid / a.nsplit;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
   const int qsub = wave & 1, kp = (wave >> 1) & 1, dhalf = wave >> 2;
+  const int partner = wave ^ 4;
 
   const size_t off = (size_t)bh * (size_t)a.S * D;
   const bf16* __restrict__ Q = a.q + off;
@@ -98,130 +140,131 @@ __global__ __launch_bounds__(NT, 1) void profile_partial_kernel(ProfileArgs a) {
   const int32_t ke = min(a.S, ks + a.keys_per_split);
   const int32_t ntiles = (ke - ks + TILE - 1) / TILE;
 
-  TileStager<D, TILE, NT> stage;
+  // two register stages: tile t+2 is fetched while tile t is computed and tile t+1 waits in
+  // registers for its LDS buffer, so two tiles per workgroup are in flight from HBM
+  TileStager<D, TILE, NT> stage_a, stage_b;
   SoftmaxState<NDBW> st[3];
   float m_ref = -INFINITY;     // reference max (log2 units) shared by the three states
+  float l[3] = {0.f, 0.f, 0.f};   // this wavefront's half of the row sums
 #pragma unroll
-  for (int x = 0; x < 3; ++x) {
-    st[x].l = 0.f;
+  for (int x = 0; x < 3; ++x)
 #pragma unroll
     for (int j = 0; j < NDBW; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) st[x].o[j][r] = 0.f;
-  }
+  bf16x8 pown[3];              // this wavefront's P^T of the previous tile
   const float c = a.scale * 1.44269504088896340736f;
   const int tg = lane >> 4, ti = lane & 15;
   const int v_row = 4 * (tg >> 1) + (ti >> 2);
   const int v_col = 16 * (tg & 1) + 4 * (ti & 3) + dhalf * (D / 2);
 
   if (ntiles > 0) {
-    stage.load(K, V, ks, a.S, tid);
-    stage.template store<KS, VS>(Ks[0], Vs[0], tid);
+    stage_a.load(K, V, ks, a.S, tid);
+    stage_a.template store<KS, VS>(Ks[0], Vs[0], tid);
   }
+  // Fetches are unconditional (past the last tile they repeat it, and nothing stores that copy):
+  // a conditional fetch would make the compiler wait for every load in flight before storing
+  // the older stage.
+  const int32_t t_last = max(ntiles - 1, 0);
+  stage_b.load(K, V, ks + min(1, t_last) * TILE, a.S, tid);
   __syncthreads();
-  for (int32_t t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    const bool has_next = t + 1 < ntiles;
-    if (has_next) stage.load(K, V, ks + (t + 1) * TILE, a.S, tid);
+  // step t: fetch tile t+2 into `fetch`, compute, then move tile t+1 from `ready` into LDS
+  auto step = [&](int32_t t, TileStager<D, TILE, NT>& fetch, TileStager<D, TILE, NT>& ready) {
+    fetch.load(K, V, ks + min(t + 2, t_last) * TILE, a.S, tid);
 
-    f32x16 sacc;
+    // ---- PV of tile t-1: own P^T for key step dhalf, the partner's for the other ----
+    if (t >= 1) {
+      bf16x8 pq3[3];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+      for (int x = 0; x < 3; ++x) pq3[x] = Px[(t - 1) & 1][partner][x][lane];
+      const bf16* vt = Vs[(t - 1) % 3];
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) {
-      const bf16x8 ak = *reinterpret_cast<const bf16x8*>(&Ks[buf][(kp * 32 + l32) * KS + 16 * s + 8 * hh]);
-      const bf16x8 bq = *reinterpret_cast<const bf16x8*>(&Qs[(qsub * 32 + l32) * KS + 16 * s + 8 * hh]);
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, bq, sacc, 0, 0, 0);
+      for (int s = 0; s < 2; ++s) {
+        const bf16* vb = &vt[(kp * 32 + 16 * s + v_row) * VS + v_col];
+        const bool mine = s == dhalf;
+#pragma unroll
+        for (int j = 0; j < NDBW; ++j) {
+          const bf16x8 av = load_vt(vb + j * 32, VS);
+#pragma unroll
+          for (int x = 0; x < 3; ++x)
+            st[x].o[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, mine ? pown[x] : pq3[x], st[x].o[j], 0, 0, 0);
+        }
+      }
     }
 
-    const int32_t kbase = ks + t * TILE + kp * 32 + 4 * hh;
-    // keys past the split's end (last tile only) do not exist
-    if (ks + (t + 1) * TILE > ke) {
+    if (t < ntiles) {
+      const int buf = t & 1;
+      f32x16 sacc;
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (kbase + 8 * (r >> 2) + (r & 3) >= ke) sacc[r] = -INFINITY;
-    }
-    // shared reference max with lazy rescaling of all three states
-    float mx = -INFINITY;
+      for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
-    const bool bump = mx > m_ref + RESCALE_SLACK;
-    if (__any(bump)) {
-      const float m_new = bump ? mx : m_ref;
-      const float alpha = (m_ref == -INFINITY) ? 0.f : exp2f(m_ref - m_new);
-#pragma unroll
-      for (int x = 0; x < 3; ++x) {
-        st[x].l *= alpha;
-#pragma unroll
-        for (int j = 0; j < NDBW; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) st[x].o[j][r] *= alpha;
+      for (int s = 0; s < NKS; ++s) {
+        const bf16x8 ak = *reinterpret_cast<const bf16x8*>(&Ks[buf][(kp * 32 + l32) * KS + 16 * s + 8 * hh]);
+        const bf16x8 bq = *reinterpret_cast<const bf16x8*>(&Qs[(qsub * 32 + l32) * KS + 16 * s + 8 * hh]);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, bq, sacc, 0, 0, 0);
       }
-      m_ref = m_new;
-    }
-    const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-    // masks as unsigned range tests: spatial key - sp_lo < sp_hi - sp_lo (frame-major keys),
-    // temporal |p_key - p_query| <= w_p on in-frame positions
-    const uint32_t sp_base = (uint32_t)(kbase - sp_lo), sp_span = (uint32_t)(sp_hi - sp_lo);
-    const int32_t pbase = PBIG ? (int32_t)fmod_((uint32_t)kbase, a.divP) : 0;
-    const uint32_t tp_span = (uint32_t)(2 * a.w_p);
-    float pd[16], psp[16], ptp[16];
-    float ld = 0.f, lsp = 0.f, ltp = 0.f;
+      const int32_t kbase = ks + t * TILE + kp * 32 + 4 * hh;
+      // keys past the split's end (last tile only) do not exist
+      if (ks + (t + 1) * TILE > ke) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int32_t dk = 8 * (r >> 2) + (r & 3);
-      int32_t pk;
-      if constexpr (PBIG) {
-        pk = pbase + dk;
-        pk -= (pk >= a.P) ? a.P : 0;
-      } else {
-        pk = (int32_t)fmod_((uint32_t)(kbase + dk), a.divP);
+        for (int r = 0; r < 16; ++r)
+          if (kbase + 8 * (r >> 2) + (r & 3) >= ke) sacc[r] = -INFINITY;
       }
-      const bool in_sp = sp_base + (uint32_t)dk < sp_span;
-      const bool in_tp = (uint32_t)(pk - pq + a.w_p) <= tp_span;
-      const float pr = __builtin_amdgcn_exp2f(fmaf(sacc[r], c, -m_use));
-      pd[r] = pr;
-      psp[r] = in_sp ? pr : 0.f;
-      ptp[r] = in_tp ? pr : 0.f;
-      ld += pd[r];
-      lsp += psp[r];
-      ltp += ptp[r];
-    }
-    st[0].l += ld;
-    st[1].l += lsp;
-    st[2].l += ltp;
-
+      // shared reference max (over all 32 keys, in both wavefronts of the pair) with lazy
+      // rescaling of all three states; the accumulators hold the products up to tile t-1
+      float mx = -INFINITY;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      bf16x8 b0, b1, b2;
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
+      const bool bump = mx > m_ref + RESCALE_SLACK;
+      if (__any(bump)) {
+        const float m_new = bump ? mx : m_ref;
+        const float alpha = (m_ref == -INFINITY) ? 0.f : exp2f(m_ref - m_new);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        b0[e] = (bf16)pd[8 * s + e];
-        b1[e] = (bf16)psp[8 * s + e];
-        b2[e] = (bf16)ptp[8 * s + e];
+        for (int x = 0; x < 3; ++x) {
+          l[x] *= alpha;
+#pragma unroll
+          for (int j = 0; j < NDBW; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) st[x].o[j][r] *= alpha;
+        }
+        m_ref = m_new;
       }
-      const bf16* vb = &Vs[buf][(kp * 32 + 16 * s + v_row) * VS + v_col];
+      const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+      // masks as unsigned range tests: spatial key - sp_lo < sp_hi - sp_lo (frame-major keys),
+      // temporal |p_key - p_query| <= w_p on in-frame positions
+      const uint32_t sp_base = (uint32_t)(kbase - sp_lo), sp_span = (uint32_t)(sp_hi - sp_lo);
+      const int32_t pbase = PBIG ? (int32_t)fmod_((uint32_t)kbase, a.divP) : 0;
+      if (dhalf == 0)
+        half_softmax<0, PBIG>(sacc, c, m_use, kbase, sp_base, sp_span, pbase, pq, a, l, pown);
+      else
+        half_softmax<1, PBIG>(sacc, c, m_use, kbase, sp_base, sp_span, pbase, pq, a, l, pown);
 #pragma unroll
-      for (int j = 0; j < NDBW; ++j) {
-        const bf16x8 av = load_vt(vb + j * 32, VS);
-        st[0].o[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b0, st[0].o[j], 0, 0, 0);
-        st[1].o[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b1, st[1].o[j], 0, 0, 0);
-        st[2].o[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b2, st[2].o[j], 0, 0, 0);
-      }
+      for (int x = 0; x < 3; ++x) Px[t & 1][wave][x][lane] = pown[x];
     }
-    if (has_next) stage.template store<KS, VS>(Ks[buf ^ 1], Vs[buf ^ 1], tid);
+    if (t + 1 < ntiles) ready.template store<KS, VS>(Ks[(t + 1) & 1], Vs[(t + 1) % 3], tid);
     __syncthreads();
+  };
+  for (int32_t t = 0; t <= ntiles; t += 2) {
+    step(t, stage_a, stage_b);
+    if (t + 1 > ntiles) break;
+    step(t + 1, stage_b, stage_a);
   }
 
-  // ---- write this wavefront's partial states (its half of the head dim) ----
+  // ---- row sums of the pair, then this wavefront's partial states (its half of the head dim)
+  float* lx = reinterpret_cast<float*>(&Px[0][0][0][0]);     // reused: [NT / 64][3][64]
+#pragma unroll
+  for (int x = 0; x < 3; ++x) lx[(wave * 3 + x) * 64 + lane] = l[x];
+  __syncthreads();
+#pragma unroll
+  for (int x = 0; x < 3; ++x) l[x] += lx[(partner * 3 + x) * 64 + lane];
   const int32_t nparts = 2 * a.nsplit;
   const int32_t part = split * 2 + kp;
   const int32_t qpad = a.n_zq * QG;
   const int32_t qloc = zq * QG + qsub * 32 + l32;
 #pragma unroll
   for (int x = 0; x < 3; ++x) {
-    const float l_tot = st[x].l + __shfl_xor(st[x].l, 32, 64);
+    const float l_tot = l[x] + __shfl_xor(l[x], 32, 64);
     const size_t slot = (((size_t)bh * nparts + part) * 3 + x) * qpad + qloc;
     if (hh == 0 && dhalf == 0) {
       a.part_ml[slot * 2 + 0] = m_ref;
