@@ -7,7 +7,7 @@
 //
 // HBM-bound: each row is read once and written once (2 x D x 2 bytes), everything else is
 // register or LDS work.  D/8 lanes own a row (8 channels = one 16-byte vector each); the
-// sum of squares is reduced across those lanes with cross-lane shuffles.  The cos/sin of
+// sum of squares is reduced across those lanes with DPP lane permutations.  The cos/sin of
 // every (axis, position, pair) -- F*dt/2 + HH*dh/2 + WW*dw/2 entries -- are computed once
 // per block in fp64 and kept in LDS as fp32 pairs, so no transcendental runs per element.
 #include "svg_internal.h"
@@ -17,10 +17,26 @@ namespace svg {
 namespace {
 
 constexpr int ROPE_THREADS = 256;
-constexpr int ROPE_UNROLL = 4;     // rows in flight per lane
+constexpr int ROPE_UNROLL = 2;     // rows per lane and batch (two batches in flight)
 
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t h) {
   return __uint_as_float(h << 16);
+}
+
+// v + the value of lane (l ^ m) within groups of four lanes, or mirrored within a row of 8 or
+// 16 lanes, through DPP (no LDS round trip)
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// sum over the N (8 or 16) consecutive lanes of a row group; every lane gets the total
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  v = dpp_add<0xB1>(v);      // quad_perm [1,0,3,2]: pairs
+  v = dpp_add<0x4E>(v);      // quad_perm [2,3,0,1]: quads
+  v = dpp_add<0x141>(v);     // row_half_mirror: groups of 8
+  if constexpr (N == 16) v = dpp_add<0x140>(v);   // row_mirror: groups of 16
+  return v;
 }
 
 template <int D>
@@ -66,13 +82,17 @@ __global__ __launch_bounds__(ROPE_THREADS) void qknorm_rope_kernel(RopeArgs a) {
   const int64_t stride = (int64_t)gridDim.x * RPP;
   const float inv_d = 1.0f / (float)D;
 
-  for (int64_t base = (int64_t)blockIdx.x * RPP + tid / LPR; base < total; base += stride * ROPE_UNROLL) {
-    u32x4 raw[ROPE_UNROLL];
+  // Batches of ROPE_UNROLL rows per lane, software-pipelined: the next batch is loaded before
+  // the current one is processed.  The loads are unconditional (rows past the end repeat the
+  // last row and are not stored), so the compiler can wait for the older batch only.
+  auto load = [&](u32x4 (&raw)[ROPE_UNROLL], int64_t base) {
 #pragma unroll
     for (int u = 0; u < ROPE_UNROLL; ++u) {
-      const int64_t row = base + u * stride;
-      if (row < total) raw[u] = in[row * LPR + lane_c];
+      const int64_t row = min(base + u * stride, total - 1);
+      raw[u] = in[row * LPR + lane_c];
     }
+  };
+  auto process = [&](const u32x4 (&raw)[ROPE_UNROLL], int64_t base) {
 #pragma unroll
     for (int u = 0; u < ROPE_UNROLL; ++u) {
       const int64_t row = base + u * stride;
@@ -88,8 +108,7 @@ __global__ __launch_bounds__(ROPE_THREADS) void qknorm_rope_kernel(RopeArgs a) {
       float ss = 0.f;
 #pragma unroll
       for (int c = 0; c < 8; ++c) ss = fmaf(x[c], x[c], ss);
-#pragma unroll
-      for (int m = LPR / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+      ss = group_sum<LPR>(ss);
       const float rs = rsqrtf(ss * inv_d + a.eps);
 
       const uint32_t tok = (uint32_t)(row - (int64_t)fdiv((uint32_t)row, a.divS) * a.S);
@@ -110,6 +129,18 @@ __global__ __launch_bounds__(ROPE_THREADS) void qknorm_rope_kernel(RopeArgs a) {
       }
       out[row * LPR + lane_c] = __builtin_bit_cast(u32x4, o);
     }
+  };
+
+  const int64_t step = stride * ROPE_UNROLL;
+  u32x4 ra[ROPE_UNROLL], rb[ROPE_UNROLL];
+  int64_t base = (int64_t)blockIdx.x * RPP + tid / LPR;
+  load(ra, base);
+  for (; base < total; base += 2 * step) {
+    load(rb, base + step);
+    process(ra, base);
+    if (base + step >= total) break;
+    load(ra, base + 2 * step);
+    process(rb, base + step);
   }
 }
 
@@ -119,10 +150,10 @@ hipError_t launch_qknorm_rope(const RopeArgs& a, hipStream_t st) {
   const size_t lds = sizeof(float2) * (size_t)(a.F * (a.dt / 2) + a.HH * (a.dh / 2) + a.WW * (a.dw / 2));
   const int64_t total = (int64_t)a.BH * a.S;
   const int rpp = ROPE_THREADS / (a.D / 8);
-  // a persistent grid of two blocks per CU and tensor, so that each block builds its
-  // cos/sin tables once and then streams many rows
+  // a persistent grid of one block per CU and tensor, so that each block builds its cos/sin
+  // tables once and then streams many rows (more blocks measured slower)
   int64_t blocks = (total + rpp * ROPE_UNROLL - 1) / (rpp * ROPE_UNROLL);
-  if (blocks > 512) blocks = 512;
+  if (blocks > 256) blocks = 256;
   const dim3 grid((unsigned)blocks, 2);
   if (a.D == 128) {
     qknorm_rope_kernel<128><<<grid, ROPE_THREADS, lds, st>>>(a);
