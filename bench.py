@@ -2,10 +2,14 @@
 """Benchmark of the sparse 3D attention path at the HunyuanVideo-720p token grid on one MI355X.
 
 A step is one layer of the path over one batch of synthetic activations already resident in
-HBM: QK-RMSNorm + 3D RoPE -> per-head profiling on 64 sampled queries -> token-major copies
-of the temporal heads' Q/K/V -> block-sparse attention -> frame-major output.  Steps cycle
-over 4 layers of fresh seeded inputs (B=1, H=24, F=33 x 45 x 80 tokens = 118800, D=128,
-bf16, half the heads planted spatial and half temporal; w_f = 1 frame, w_p = 64 positions).
+HBM: QK-RMSNorm + 3D RoPE -> per-head profiling on 64 sampled queries -> layout
+transformation of the temporal heads -> block-sparse attention -> frame-major output.  With
+--layout fused (the default) the attention kernel applies the layout transformation as it
+loads and stores rows; with --layout explicit the step materialises token-major copies of
+Q/K/V (svg_permute) and restores the output (svg_unpermute).  The other layout is timed too
+(unless --no-compare) and reported under "compare".  Steps cycle over 4 layers of fresh
+seeded inputs (B=1, H=24, F=33 x 45 x 80 tokens = 118800, D=128, bf16, half the heads
+planted spatial and half temporal; w_f = 1 frame, w_p = 64 positions).
 
 Prints one JSON line on stdout (progress goes to stderr).  `value` is the effective
 attention throughput of the whole step: FLOPs of the computed attention tiles (4*D per
@@ -39,6 +43,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=12)
     ap.add_argument("--warmup", type=int, default=4)
     ap.add_argument("--layers", type=int, default=4)
+    ap.add_argument("--layout", choices=("fused", "explicit"), default="fused",
+                    help="layout transformation of temporal heads inside the attention kernel, or as separate "
+                         "permute / unpermute passes")
+    ap.add_argument("--no-compare", action="store_true", help="do not also time the other layout")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (the reference kernel that scales "
                          "the FETCH_SIZE / WRITE_SIZE counters to bytes) and exit")
@@ -161,7 +169,7 @@ def main():
     bm, bn = svg.tile_shape()
     F, HH, WW, w_f, w_p = g.F, g.HH, g.WW, wl.w_f, wl.w_p
 
-    def step(l, ev=None):
+    def step(l, ev=None, layout=args.layout):
         q, k, v, idx = layers[l]
         if ev is not None:
             ev[0].record()
@@ -171,16 +179,21 @@ def main():
         svg.profile_heads(qn, kn, v, idx, F, HH, WW, w_f, w_p, mse=bufs.mse, kind=bufs.kind, ws=bufs.ws_profile)
         if ev is not None:
             ev[2].record()
-        svg.permute(qn, F, HH, WW, bufs.kind, svg.TEMPORAL, out=bufs.qt)
-        svg.permute(kn, F, HH, WW, bufs.kind, svg.TEMPORAL, out=bufs.kt)
-        svg.permute(v, F, HH, WW, bufs.kind, svg.TEMPORAL, out=bufs.vt)
+        if layout == "explicit":
+            svg.permute(qn, F, HH, WW, bufs.kind, svg.TEMPORAL, out=bufs.qt)
+            svg.permute(kn, F, HH, WW, bufs.kind, svg.TEMPORAL, out=bufs.kt)
+            svg.permute(v, F, HH, WW, bufs.kind, svg.TEMPORAL, out=bufs.vt)
         if ev is not None:
             ev[3].record()
-        svg.sparse_attn(qn, kn, v, bufs.qt, bufs.kt, bufs.vt, bufs.kind, F, HH, WW, w_f, w_p, o=bufs.o, ot=bufs.ot,
-                        ws=bufs.ws_attn)
+        if layout == "explicit":
+            svg.sparse_attn(qn, kn, v, bufs.qt, bufs.kt, bufs.vt, bufs.kind, F, HH, WW, w_f, w_p, o=bufs.o,
+                            ot=bufs.ot, ws=bufs.ws_attn)
+        else:
+            svg.sparse_attn(qn, kn, v, None, None, None, bufs.kind, F, HH, WW, w_f, w_p, o=bufs.o, ws=bufs.ws_attn)
         if ev is not None:
             ev[4].record()
-        svg.unpermute(bufs.ot, F, HH, WW, bufs.kind, svg.TEMPORAL, out=bufs.o)
+        if layout == "explicit":
+            svg.unpermute(bufs.ot, F, HH, WW, bufs.kind, svg.TEMPORAL, out=bufs.o)
         if ev is not None:
             ev[5].record()
 
@@ -200,17 +213,31 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps")
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i % L, evs[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    stage = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(5)] for i in range(args.steps)])
     names = ["qknorm_rope", "profile_heads", "permute_qkv", "sparse_attn", "unpermute"]
+
+    def timed(layout):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(i % L, evs[i], layout)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        st = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(5)] for i in range(args.steps)])
+        return (t1 - t0) * 1e3 / args.steps, st
+
+    ms_per_step, stage = timed(args.layout)
     stage_ms = {n: float(stage[:, j].mean()) for j, n in enumerate(names)}
+    other = "explicit" if args.layout == "fused" else "fused"
+    compare = None
+    if not args.no_compare:
+        for i in range(args.warmup):
+            step(i % L, None, other)
+        o_ms, o_stage = timed(other)
+        compare = {"layout": other, "ms_per_step": round(o_ms, 4),
+                   "stage_ms": {n: round(float(o_stage[:, j].mean()), 4) for j, n in enumerate(names)}}
+        log(f"[bench] {other} layout: {o_ms:.3f} ms/step")
+    ex_stage = stage if args.layout == "explicit" else (o_stage if compare else None)
     step_tile = np.array([flops_tile[i % L] for i in range(args.steps)])
     step_tok = np.array([flops_tok[i % L] for i in range(args.steps)])
     attn_ms = stage[:, 3]
@@ -223,10 +250,11 @@ def main():
     row = S * D * 2
     hbm = {
         "qknorm_rope": float(np.mean(4 * BH * row / (stage[:, 0] * 1e-3)) / 1e9),
-        "permute_qkv": float(np.mean(6 * n_tmp * row / (stage[:, 2] * 1e-3)) / 1e9),
-        "unpermute": float(np.mean(2 * n_tmp * row / (stage[:, 4] * 1e-3)) / 1e9),
         "profile_heads": float(np.mean(2 * BH * row / (stage[:, 1] * 1e-3)) / 1e9),
     }
+    if ex_stage is not None:   # the separate layout passes, from the explicit-layout steps
+        hbm["permute_qkv"] = float(np.mean(6 * n_tmp * row / (ex_stage[:, 2] * 1e-3)) / 1e9)
+        hbm["unpermute"] = float(np.mean(2 * n_tmp * row / (ex_stage[:, 4] * 1e-3)) / 1e9)
 
     # the same kernel run dense, on layer 0
     q, k, v, _ = layers[0]
@@ -254,8 +282,10 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "hunyuan720p_step: one layer (qknorm+rope, profile 64 queries, permute, "
-                               "block-sparse attention, unpermute) over 4 layers of fresh inputs",
+        "config": {"workload": "hunyuan720p_step: one layer (qknorm+rope, profile 64 queries, layout "
+                               "transformation of temporal heads, block-sparse attention) over 4 layers of "
+                               "fresh inputs",
+                   "layout": args.layout,
                    "B": g.B, "H": g.H, "F": g.F, "HH": g.HH, "WW": g.WW, "S": S, "D": D, "w_f": w_f, "w_p": w_p,
                    "n_q": wl.n_q, "layers": L, "tile": [bm, bn], "parallelism": "single GPU"},
         "sparse_attn_ms": round(float(attn_ms.mean()), 4),
@@ -269,6 +299,7 @@ def main():
         "speedup_vs_dense_step": round((stage_ms["qknorm_rope"] + dense_ms) / ms_per_step, 3),
         "profile_over_attn": round(stage_ms["profile_heads"] / stage_ms["sparse_attn"], 4),
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "compare": compare,
         "hbm_gbs": {k: round(v, 1) for k, v in hbm.items()},
         "hbm_frac_of_peak": {k: round(v / PEAK_HBM_GBS, 3) for k, v in hbm.items()},
         "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel<128>", "achieved": round(attn_tflops, 2),

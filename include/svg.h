@@ -142,14 +142,20 @@ svg_status svg_build_block_mask(const uint8_t* kind, svg_geom g, svg_windows w, 
  * [svg-authors] Layout Transformation / [svg-jqzx] kernel section: the sparse kernel only
  * computes the tiles the pattern needs.  Per head, in its working layout:
  *   O = softmax(scale * Q K^T  restricted to the head's token mask) V
- * Spatial and dense heads read q, k, v (frame-major) and write o; temporal heads read qt,
- * kt, vt (token-major, e.g. from svg_permute) and write ot (token-major; restore with
- * svg_unpermute).  Tiles outside the mask are skipped; inside boundary tiles the exact
- * token mask is applied.  bf16 inputs, fp32 accumulation, bf16 output.
- * q, k, v, o, qt, kt, vt, ot: bf16 [B][H][S][D]; the token-major ones may be NULL when no
- * head is temporal only if kind is NULL.
+ * Spatial and dense heads read q, k, v (frame-major) and write o.  Temporal heads work in
+ * token-major order, in one of two ways:
+ *   - qt, kt, vt, ot all non-NULL: they read qt, kt, vt (token-major, e.g. from svg_permute)
+ *     and write ot (token-major; restore with svg_unpermute);
+ *   - qt, kt, vt, ot all NULL (fused layout transformation): they read q, k, v and write o,
+ *     frame-major, and the kernel applies the permutation as it loads and stores rows.
+ *     Results are bit-identical to the first way followed by svg_unpermute.
+ * Tiles outside the mask are skipped; inside boundary tiles the exact token mask is
+ * applied.  bf16 inputs, fp32 accumulation, bf16 output.
+ * q, k, v, o, qt, kt, vt, ot: bf16 [B][H][S][D]; a mix of NULL and non-NULL token-major
+ * pointers is SVG_ERR_INVALID when kind is given (they are ignored when kind is NULL).
  * kind: uint8 [B*H] device array (NULL = every head dense).
  * ws:   >= svg_workspace_bytes(SVG_OP_SPARSE_ATTN, &g, 0) bytes.
+ * S*D*2 bytes (one head) must be below 4 GB, else SVG_ERR_UNSUPPORTED (also svg_dense_attn).
  */
 svg_status svg_sparse_attn(const void* q, const void* k, const void* v,
                            const void* qt, const void* kt, const void* vt,

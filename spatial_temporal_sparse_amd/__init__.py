@@ -225,16 +225,22 @@ def build_block_mask(kind, F, HH, WW, w_f, w_p, bm, bn):
 
 def sparse_attn(q, k, v, qt, kt, vt, kind, F, HH, WW, w_f, w_p, scale=None, o=None, ot=None, ws=None):
     """Block-sparse attention (svg_sparse_attn): spatial/dense heads read q/k/v and write o
-    (frame-major); temporal heads read qt/kt/vt and write ot (token-major).  Returns (o, ot)."""
+    (frame-major); temporal heads read qt/kt/vt and write ot (token-major).  With qt, kt, vt
+    all None the layout transformation is fused: temporal heads read q/k/v and write o too,
+    and ot is None.  Returns (o, ot)."""
     g = geometry(q, F, HH, WW)
     shp = _shape(g)
-    for n, t in (("q", q), ("k", k), ("v", v), ("qt", qt), ("kt", kt), ("vt", vt)):
+    fused = qt is None and kt is None and vt is None
+    if fused and ot is not None:
+        raise ValueError("ot must be None when qt, kt and vt are None (fused layout transformation)")
+    for n, t in (("q", q), ("k", k), ("v", v)) + (() if fused else (("qt", qt), ("kt", kt), ("vt", vt))):
         _check_qkv(n, t, shp, device=q.device)
     _check_qkv("kind", kind, (g.B, g.H), torch.uint8, q.device)
     o = torch.empty_like(q) if o is None else o
-    ot = torch.empty_like(q) if ot is None else ot
+    if not fused:
+        ot = torch.empty_like(q) if ot is None else ot
+        _check_qkv("ot", ot, shp, device=q.device)
     _check_qkv("o", o, shp, device=q.device)
-    _check_qkv("ot", ot, shp, device=q.device)
     ws = _workspace(OP_SPARSE_ATTN, g, 0, q.device, ws)
     sc = default_scale(g.D) if scale is None else scale
     _check(lib.svg_sparse_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(qt), _ptr(kt), _ptr(vt), _ptr(kind), g,
@@ -271,10 +277,12 @@ class LayerBuffers:
         self.ws_attn = torch.empty(max(256, workspace_bytes(OP_SPARSE_ATTN, g, 0)), dtype=torch.uint8, device=dev)
 
 
-def sparse_layer(q, k, v, q_idx, F, HH, WW, w_f, w_p, norm=None, scale=None, bufs: Optional[LayerBuffers] = None):
+def sparse_layer(q, k, v, q_idx, F, HH, WW, w_f, w_p, norm=None, scale=None, bufs: Optional[LayerBuffers] = None,
+                 fused=False):
     """One layer of the path, all on the current stream with no host synchronisation:
     [QK-RMSNorm + 3D RoPE] -> profile heads -> token-major copies of temporal heads' Q/K/V ->
-    block-sparse attention -> frame-major output.
+    block-sparse attention -> frame-major output.  fused=True leaves the layout transformation
+    to the attention kernel's loads and stores (same result, no copies).
 
     norm: None or (wq, wk, eps, rope_base).  Returns (o, kind, mse, q', k').
     """
@@ -284,6 +292,9 @@ def sparse_layer(q, k, v, q_idx, F, HH, WW, w_f, w_p, norm=None, scale=None, buf
         wq, wk, eps, base = norm
         q, k = qknorm_rope(q, k, wq, wk, F, HH, WW, eps, base, q_out=bufs.qn, k_out=bufs.kn)
     profile_heads(q, k, v, q_idx, F, HH, WW, w_f, w_p, scale, mse=bufs.mse, kind=bufs.kind, ws=bufs.ws_profile)
+    if fused:
+        sparse_attn(q, k, v, None, None, None, bufs.kind, F, HH, WW, w_f, w_p, scale, o=bufs.o, ws=bufs.ws_attn)
+        return bufs.o, bufs.kind, bufs.mse, q, k
     permute(q, F, HH, WW, bufs.kind, TEMPORAL, out=bufs.qt)
     permute(k, F, HH, WW, bufs.kind, TEMPORAL, out=bufs.kt)
     permute(v, F, HH, WW, bufs.kind, TEMPORAL, out=bufs.vt)

@@ -229,6 +229,14 @@ SVG_API svg_status svg_build_block_mask(const uint8_t* kind, svg_geom g, svg_win
   return hip_status(svg::launch_block_mask(a, (hipStream_t)stream), "svg_build_block_mask");
 }
 
+// The attention kernel addresses a head's rows with 32-bit byte offsets.
+static svg_status check_head_bytes(const svg_geom& g) {
+  const int64_t S = (int64_t)g.F * g.HH * g.WW;
+  if (S * g.D * 2 >= ((int64_t)1 << 32))
+    return fail(SVG_ERR_UNSUPPORTED, "one head of S=%lld rows x D=%d exceeds 4 GB", (long long)S, g.D);
+  return SVG_OK;
+}
+
 static void fill_attn(svg::AttnArgs& a, svg_geom g, svg_windows w, float scale) {
   a.BH = g.B * g.H;
   a.S = g.F * g.HH * g.WW;
@@ -249,9 +257,12 @@ SVG_API svg_status svg_sparse_attn(const void* q, const void* k, const void* v, 
   if ((s = check_geom(g, true)) != SVG_OK) return s;
   if ((s = check_windows(w)) != SVG_OK) return s;
   if ((s = check_ptrs({{q, "q"}, {k, "k"}, {v, "v"}, {o, "o"}})) != SVG_OK) return s;
-  if (kind != nullptr) {
+  // all four token-major tensors NULL: temporal heads are read and written in place (fused)
+  const bool fused = qt == nullptr && kt == nullptr && vt == nullptr && ot == nullptr;
+  if (kind != nullptr && !fused) {
     if ((s = check_ptrs({{qt, "qt"}, {kt, "kt"}, {vt, "vt"}, {ot, "ot"}})) != SVG_OK) return s;
   }
+  if ((s = check_head_bytes(g)) != SVG_OK) return s;
   if (!(scale > 0.f) || !std::isfinite(scale)) return fail(SVG_ERR_INVALID, "scale must be finite and > 0");
   const size_t need = attn_ws_bytes(g);
   if (kind != nullptr && (ws == nullptr || ws_bytes < need))
@@ -269,6 +280,7 @@ SVG_API svg_status svg_sparse_attn(const void* q, const void* k, const void* v, 
   a.kind = kind;
   a.order = kind ? (int32_t*)ws : nullptr;
   a.force_dense = 0;
+  a.fused_t = fused ? 1 : 0;
   fill_attn(a, g, w, scale);
   return hip_status(svg::launch_attention(a, (hipStream_t)stream), "svg_sparse_attn");
 }
@@ -278,8 +290,10 @@ SVG_API svg_status svg_dense_attn(const void* q, const void* k, const void* v, s
   svg_status s;
   if ((s = check_geom(g, true)) != SVG_OK) return s;
   if ((s = check_ptrs({{q, "q"}, {k, "k"}, {v, "v"}, {o, "o"}})) != SVG_OK) return s;
+  if ((s = check_head_bytes(g)) != SVG_OK) return s;
   if (!(scale > 0.f) || !std::isfinite(scale)) return fail(SVG_ERR_INVALID, "scale must be finite and > 0");
   svg::AttnArgs a;
+  a.fused_t = 0;
   a.q = a.qt = (const svg::bf16*)q;
   a.k = a.kt = (const svg::bf16*)k;
   a.v = a.vt = (const svg::bf16*)v;

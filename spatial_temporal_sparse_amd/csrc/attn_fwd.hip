@@ -264,24 +264,40 @@ __device__ __forceinline__ void phase_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Row of the tensor in memory that holds row u of the head's working layout: u itself, or
+// for a temporal head read in place (fused layout transformation) the frame-major row of
+// token-major row u = p*F + f, namely f*P + p.
+struct RowMap {
+  FastDiv divF;
+  int32_t F, P;
+  bool tm;                     // u is token-major, memory is frame-major
+  __device__ __forceinline__ int32_t operator()(int32_t u) const {
+    if (!tm) return u;
+    const int32_t p = (int32_t)fdiv((uint32_t)u, divF);
+    return (u - p * F) * P + p;
+  }
+};
+
 // Copy of one K or V tile into LDS by the four wavefronts of one group (wb = 0..3): per
-// wavefront, PER_WAVE instructions of 1 KB each.  The address is a wavefront-uniform tile base
-// plus a 32-bit per-lane offset; rows past the sequence end repeat its last row.
+// wavefront, PER_WAVE instructions of 1 KB each.  The address is the wavefront-uniform head
+// base plus a 32-bit per-lane offset (the host checks that a head fits in 4 GB); rows past
+// the sequence end repeat its last row.  Every lane copies 16 bytes of one row, so the rows
+// of a tile may come from anywhere: the row map gathers them.
 template <int D>
 __device__ __forceinline__ void pp_load(const bf16* __restrict__ src, int32_t k0, int32_t S, bf16* dst, int wb,
-                                        int lane, bool is_v) {
+                                        int lane, bool is_v, const RowMap& rmap) {
   using T = TileLds<D>;
   constexpr int PER_WAVE = T::TILE_BYTES / 1024 / 4;
   constexpr int RPI = 1024 / T::ROW_BYTES;                // tile rows per instruction
-  const bf16* tile = src + (size_t)k0 * D;
   const int pc = lane % T::CPR;
 #pragma unroll
   for (int i = 0; i < PER_WAVE; ++i) {
     const int kb = (wb * PER_WAVE + i) * 1024;
     const int row = (wb * PER_WAVE + i) * RPI + lane / T::CPR;
     const int lc = pc ^ (is_v ? T::swz_v(row) : T::swz_k(row));
-    const uint32_t off = (uint32_t)(min(row, S - 1 - k0) * D + 8 * lc);
-    __builtin_amdgcn_global_load_lds(tile + off, (__attribute__((address_space(3))) void*)((char*)dst + kb), 16, 0, 0);
+    const uint32_t boff = (uint32_t)rmap(min(k0 + row, S - 1)) * (uint32_t)T::ROW_BYTES + 16u * (uint32_t)lc;
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(src) + boff,
+                                     (__attribute__((address_space(3))) void*)((char*)dst + kb), 16, 0, 0);
   }
 }
 
@@ -300,11 +316,19 @@ __global__ __launch_bounds__(PP_NT, 1) void attn_fwd_kernel(AttnArgs a, int32_t 
   int kind = (a.force_dense || a.kind == nullptr) ? KIND_DENSE : (int)a.kind[bh];
   if (kind != KIND_SPATIAL && kind != KIND_TEMPORAL) kind = KIND_DENSE;
   const bool tmaj = kind == KIND_TEMPORAL;
+  // temporal heads work in token-major order; they read token-major copies (qt, kt, vt -> ot)
+  // or, fused, the frame-major tensors through the row map
+  const bool own_t = tmaj && !a.fused_t;
   const size_t off = (size_t)bh * (size_t)a.S * D;
-  const bf16* __restrict__ Q = (tmaj ? a.qt : a.q) + off;
-  const bf16* __restrict__ K = (tmaj ? a.kt : a.k) + off;
-  const bf16* __restrict__ V = (tmaj ? a.vt : a.v) + off;
-  bf16* __restrict__ O = (tmaj ? a.ot : a.o) + off;
+  const bf16* __restrict__ Q = (own_t ? a.qt : a.q) + off;
+  const bf16* __restrict__ K = (own_t ? a.kt : a.k) + off;
+  const bf16* __restrict__ V = (own_t ? a.vt : a.v) + off;
+  bf16* __restrict__ O = (own_t ? a.ot : a.o) + off;
+  RowMap rmap;
+  rmap.divF = a.divF;
+  rmap.F = a.F;
+  rmap.P = a.P;
+  rmap.tm = tmaj && a.fused_t;
 
   Band band;
   band.S = a.S;
@@ -346,12 +370,12 @@ __global__ __launch_bounds__(PP_NT, 1) void attn_fwd_kernel(AttnArgs a, int32_t 
   band_interval(band, my_qc, my_lo, my_hi);
 
   // first tiles: K(t_0) by group A, V(t_0) by group B
-  if (grp == 0) pp_load<D>(K, t_begin * BN, a.S, K0, wig, lane, false);
-  else pp_load<D>(V, t_begin * BN, a.S, Vb[0], wig, lane, true);
+  if (grp == 0) pp_load<D>(K, t_begin * BN, a.S, K0, wig, lane, false, rmap);
+  else pp_load<D>(V, t_begin * BN, a.S, Vb[0], wig, lane, true, rmap);
   bf16x8 qf[NKS];
 #pragma unroll
   for (int s = 0; s < NKS; ++s)
-    qf[s] = *reinterpret_cast<const bf16x8*>(Q + (size_t)my_qc * D + 16 * s + 8 * hh);
+    qf[s] = *reinterpret_cast<const bf16x8*>(Q + (size_t)rmap(my_qc) * D + 16 * s + 8 * hh);
 
   RowState<D> st;
 #pragma unroll
@@ -394,10 +418,10 @@ __global__ __launch_bounds__(PP_NT, 1) void attn_fwd_kernel(AttnArgs a, int32_t 
   };
   // copies after M(j): group A K(t_{j+1}) -> kdst, group B V(t_{j+1}) -> Vb[(j+1) % 3]
   auto copy_k = [&](int32_t j, bf16* kdst) {
-    if (j + 1 < T) pp_load<D>(K, (t_begin + j + 1) * BN, a.S, kdst, wig, lane, false);
+    if (j + 1 < T) pp_load<D>(K, (t_begin + j + 1) * BN, a.S, kdst, wig, lane, false, rmap);
   };
   auto copy_v = [&](int32_t j) {
-    if (j + 1 < T) pp_load<D>(V, (t_begin + j + 1) * BN, a.S, Vb[(j + 1) % 3], wig, lane, true);
+    if (j + 1 < T) pp_load<D>(V, (t_begin + j + 1) * BN, a.S, Vb[(j + 1) % 3], wig, lane, true, rmap);
   };
   auto vbuf = [&](int32_t j) { return Vb[(j + 3) % 3]; };   // V(t_j), j >= -1
 
@@ -449,7 +473,7 @@ __global__ __launch_bounds__(PP_NT, 1) void attn_fwd_kernel(AttnArgs a, int32_t 
   if (my_q < a.S) {
     const float l_tot = st.l_run + other_half(st.l_run);
     const float inv = 1.f / l_tot;
-    bf16* orow = O + (size_t)my_q * D;
+    bf16* orow = O + (size_t)rmap(my_q) * D;
 #pragma unroll
     for (int j = 0; j < NDB; ++j)
 #pragma unroll

@@ -168,6 +168,7 @@ struct AttnArgs {
   FastDiv divP, divF;
   float scale;
   int32_t force_dense;
+  int32_t fused_t;            // temporal heads read q/k/v and write o through the permutation
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
 

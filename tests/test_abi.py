@@ -100,6 +100,15 @@ def test_argument_checks(svg):
                              None) == -1
     assert L.svg_sparse_attn(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, good, W(1, 2), 0.125, FAKE, FAKE, None, 0,
                              None) == -4
+    # all four token-major tensors NULL selects the fused layout transformation: only the
+    # workspace is missing here
+    assert L.svg_sparse_attn(FAKE, FAKE, FAKE, None, None, None, FAKE, good, W(1, 2), 0.125, FAKE, None, None, 0,
+                             None) == -4
+    # a head must fit in 4 GB (S * D * 2 bytes)
+    big = svg.Geom(1, 1, 1 << 5, 1 << 10, 1 << 10, 128)
+    assert L.svg_dense_attn(FAKE, FAKE, FAKE, big, 0.1, FAKE, None) == -2
+    assert L.svg_sparse_attn(FAKE, FAKE, FAKE, None, None, None, FAKE, big, W(1, 2), 0.125, FAKE, None, FAKE,
+                             1 << 20, None) == -2
     # rope slices must be even and add up to D; eps must be positive
     assert L.svg_qknorm_rope(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1e-6, 1e4, 24, 21, 19, good, None) == -1
     assert L.svg_qknorm_rope(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.0, 1e4, 24, 20, 20, good, None) == -1

@@ -143,3 +143,47 @@ def test_720p_sampled_rows(gpu):
         assert_close_attn(host64(o[0, h])[rows], want, f"720p h{h}")
         want_d = O.head_attention_rows(qh, kh, vh, rows[::4], O.DENSE, g.F, g.P, w_f, w_p, sc)
         assert_close_attn(host64(od[0, h])[rows[::4]], want_d, f"720p dense h{h}")
+
+
+# ---- fused layout transformation (token-major pointers NULL) ----
+
+FUSED_CASES = CASES + [
+    ("cogvideox_like", Geometry(1, 6, 13, 30, 45, 64), (1, 8), True),
+    ("hunyuan_f4", Geometry(1, 4, 4, 45, 80, 128), (1, 64), True),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_fused_layout_equals_explicit_permute_bitwise(gpu, case):
+    """The fused path reads temporal heads' rows through the permutation instead of from
+    token-major copies; the arithmetic is the same, so the output must be identical."""
+    name, g, (w_f, w_p), planted = case
+    note(f"fused vs explicit layout transformation {name} {g}")
+    q, k, v = _inputs(name, g, planted, seed=31)
+    kinds = np.array([[(b + 2 * h) % 3 for h in range(g.H)] for b in range(g.B)], dtype=np.uint8)
+    want = _run_sparse(gpu, q, k, v, kinds, g, w_f, w_p)
+    kd = torch.from_numpy(kinds).to(DEV)
+    o, ot = gpu.sparse_attn(q, k, v, None, None, None, kd, g.F, g.HH, g.WW, w_f, w_p)
+    torch.cuda.synchronize()
+    assert ot is None
+    assert torch.equal(o, want)
+
+
+def test_fused_layout_vs_oracle_720p_rows(gpu):
+    """Fused path on the full 720p grid, a temporal and a spatial head, rows sampled across
+    the sequence (first and last query blocks included), against the oracle."""
+    g = Geometry(1, 2, 33, 45, 80, 128)
+    w_f, w_p = 1, 64
+    note("fused 720p grid sampled rows")
+    q, k, v = _inputs("hyfused", g, True, seed=32)
+    kinds = np.array([[O.TEMPORAL, O.SPATIAL]], dtype=np.uint8)
+    o, _ = gpu.sparse_attn(q, k, v, None, None, None, torch.from_numpy(kinds).to(DEV), g.F, g.HH, g.WW, w_f, w_p)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(8)
+    rows = np.unique(np.concatenate([rng.choice(g.S, 96, replace=False), np.arange(0, 128),
+                                     np.arange(g.S - 144, g.S)]))
+    sc = O.default_scale(g.D)
+    for h in range(2):
+        qh, kh, vh = host64(q[0, h]), host64(k[0, h]), host64(v[0, h])
+        want = O.head_attention_rows(qh, kh, vh, rows, int(kinds[0, h]), g.F, g.P, w_f, w_p, sc)
+        assert_close_attn(host64(o[0, h])[rows], want, f"fused 720p h{h}")
