@@ -5,19 +5,26 @@
 // mask; each head keeps the mask whose output has the smaller mean squared error against
 // the unmasked output.
 //
-// Pass 1 (split-K): a workgroup takes one (head, key range, group of 64 sampled queries).
-// Its eight wavefronts cover the two 32-query halves x the two 32-key halves of each 64-key
-// tile x the two halves of the head dim (for the outputs; the scores are shared work).  Per
-// tile, S^T = K Q^T on MFMA (as in the attention kernel), then three online softmax states
-// -- dense, spatial, temporal -- each with its own row sum and O^T accumulator; the three PV
-// products share the V^T operands read once from LDS.  The three states share one running
-// reference max, the unmasked one: softmax does not depend on the reference, so each masked
-// state only selects the unmasked exponentials of its keys.  This is exact up to rounding
-// while a row's masked scores stay within 126 (log2 units) of its unmasked maximum; beyond
-// that the masked exponentials underflow.
+// Pass 1 (split-K): a workgroup of four wavefronts takes one (head, key range, group of 64
+// sampled queries), 16 queries per wavefront, and two workgroups share a CU, so that one's
+// matrix products overlap the other's exponentials.  Per 32-key tile and wavefront, with
+// v_mfma_f32_16x16x32_bf16 (lane l: row/column l%16, k-quarter l/16):
+//   S^T[key][query] = K Q^T       A = K rows from LDS, B = the wavefront's Q rows, kept in
+//                                 registers; lane l holds 8 scores of query l%16.
+//   O_x^T[d][query] += V^T P_x^T  for the three softmax states x (dense, spatial, temporal):
+//                                 A = V^T from the LDS transpose read, shared by the three
+//                                 products; B = P_x^T converted to bf16 straight from the
+//                                 score registers (the key order inside the 32-key step is
+//                                 permuted identically on both operands).
+// The three states share one running reference max, the unmasked one: softmax does not
+// depend on the reference, so each masked state only selects the unmasked exponentials of
+// its keys.  This is exact up to rounding while a row's masked scores stay within 126 (log2
+// units) of its unmasked maximum; beyond that the masked exponentials underflow.
 // Keys are frame-major here: the spatial mask is a per-query interval of frames, the
-// temporal mask compares in-frame positions (key mod P).  Each wavefront writes its
-// unnormalised partial state (reference max, row sum, O) to the workspace.
+// temporal mask compares in-frame positions (key mod P).  Each wavefront writes the
+// unnormalised partial state (reference max, row sum, O) of its queries to the workspace.
+// Key and value tiles are copied HBM -> LDS (global_load_lds_dwordx4, no register staging)
+// into four buffers, three tiles ahead of their use.
 // Pass 2: one workgroup per (head, sampled row) merges that row's partial states with
 // log-sum-exp weights, forms its three outputs (one channel per thread) and sums the two
 // squared errors over the channels in fp64.
@@ -30,78 +37,205 @@ namespace svg {
 
 namespace {
 
-constexpr int NT = 512;            // partial pass
+constexpr int NT = 256;            // partial pass: four wavefronts
 constexpr int NT_RED = 256;        // reduce pass
-constexpr int TILE = 64;
-constexpr int QG = 64;           // sampled queries per workgroup
+constexpr int TILE = 32;           // keys per tile
+constexpr int NBUF = 4;            // tile buffers (copies run NBUF-1 tiles ahead)
+constexpr int QG = 64;             // sampled queries per workgroup
 constexpr int MAX_SPLIT = 128;
-constexpr int TARGET_WGS = 512;
+constexpr int TARGET_WGS = 512;    // two workgroups per CU
 constexpr float RESCALE_SLACK = 8.0f;
 
+// s_waitcnt immediate (gfx9 encoding): at most vm vector-memory loads and lgkm LDS operations
+// outstanding, exports not waited for.
+constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | (7 << 4) | ((lgkm & 15) << 8) | ((vm >> 4) << 14); }
+
+// Tile geometry in LDS: rows of D bf16 (no padding), 16-byte chunks XOR-swizzled per row.
 template <int D>
-struct PLds {
-  static constexpr int KS = D + 8;
-  static constexpr int VS = D + 32;
+struct PTile {
+  static constexpr int CPR = D / 8;            // 16-byte chunks per row
+  static constexpr int RPB = 16 / CPR;         // rows per 256-byte bank period
+  static constexpr int ROW_BYTES = D * 2;
+  static constexpr int TILE_BYTES = TILE * ROW_BYTES;
+  static constexpr int CPW = 2 * TILE_BYTES / 1024 / (NT / 64);   // 1 KB copies per wavefront and tile (K + V)
+  // K is read 16 rows x one chunk per 16 lanes: spread those rows over all 16 chunk slots.
+  static __device__ __forceinline__ int swz_k(int r) { return (r / RPB) & (CPR - 1); }
+  // V is read by the transpose read, 8 rows x two adjacent chunks per 32 lanes: give each of
+  // the 8 rows its own pair of chunk slots.
+  static __device__ __forceinline__ int swz_v(int r) { return 2 * ((r / RPB) & (CPR / 2 - 1)); }
 };
 
-// Unnormalised O^T of one softmax state (reference max and row sums are kept beside it).
-template <int NDB>
-struct SoftmaxState {
-  f32x16 o[NDB];
-};
+// value of x held by lane l^16 / l^32 combined with x by max or by sum
+__device__ __forceinline__ float max_x16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(fmaxf(x, __uint_as_float(r[0])), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_x32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(fmaxf(x, __uint_as_float(r[0])), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_x16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);   // own value in one entry, partner's in the other
+}
+__device__ __forceinline__ float sum_x32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
-// Scores -> P of one tile for one wavefront: the half DH of its 32 keys (16 keys, score
-// registers 8*DH .. 8*DH+7) in all three states, row sums of that half, bf16 P^T operands.
-// The reference max m_use is shared (see the header).
-template <int DH, bool PBIG>
-__device__ __forceinline__ void half_softmax(const f32x16& sacc, float c, float m_use, int32_t kbase, uint32_t sp_base,
-                                             uint32_t sp_span, int32_t pbase, int32_t pq, const ProfileArgs& a,
-                                             float (&l)[3], bf16x8 (&pb)[3]) {
-  const uint32_t tp_span = (uint32_t)(2 * a.w_p);
+// Copy of one K or V tile (rows k0.., clamped to S-1) into LDS by the four wavefronts: each
+// wavefront fills CPW/2 consecutive KB of the tile, every lane 16 bytes of one row.
+template <int D>
+__device__ __forceinline__ void tile_copy(const bf16* __restrict__ src, int32_t k0, int32_t S, bf16* dst, int wave,
+                                          int lane, bool is_v) {
+  using T = PTile<D>;
+  constexpr int PER = T::CPW / 2;
+  constexpr int RPI = 1024 / T::ROW_BYTES;     // tile rows per instruction
+  const int pc = lane % T::CPR;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int r = 8 * DH + e;
-    const int32_t dk = 8 * (r >> 2) + (r & 3);
-    int32_t pk;
-    if constexpr (PBIG) {
-      pk = pbase + dk;
-      pk -= (pk >= a.P) ? a.P : 0;
-    } else {
-      pk = (int32_t)fmod_((uint32_t)(kbase + dk), a.divP);
-    }
-    const bool in_sp = sp_base + (uint32_t)dk < sp_span;
-    const bool in_tp = (uint32_t)(pk - pq + a.w_p) <= tp_span;
-    const float pr = __builtin_amdgcn_exp2f(fmaf(sacc[r], c, -m_use));
-    const float ps = in_sp ? pr : 0.f;
-    const float pt = in_tp ? pr : 0.f;
-    l[0] += pr;
-    l[1] += ps;
-    l[2] += pt;
-    pb[0][e] = (bf16)pr;
-    pb[1][e] = (bf16)ps;
-    pb[2][e] = (bf16)pt;
+  for (int i = 0; i < PER; ++i) {
+    const int blk = wave * PER + i;
+    const int row = blk * RPI + lane / T::CPR;
+    const int lc = pc ^ (is_v ? T::swz_v(row) : T::swz_k(row));
+    const uint32_t boff = (uint32_t)min(k0 + row, S - 1) * (uint32_t)T::ROW_BYTES + 16u * (uint32_t)lc;
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(src) + boff,
+                                     (__attribute__((address_space(3))) void*)((char*)dst + blk * 1024), 16, 0, 0);
   }
 }
 
-// PBIG: a frame holds at least 32 tokens, so a lane's keys (a span of 28) cross at most one
+// Workgroup barrier without a memory fence (a fenced one would also wait for the copies
+// still in flight for later tiles).  The empty asm statements keep LDS accesses on their side.
+__device__ __forceinline__ void tile_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Per-lane state: three O^T accumulators (D/16 blocks of 16 channels x 16 queries each),
+// the shared reference max and the lane's shares of the three row sums.
+template <int D>
+struct PState {
+  f32x4 o[3][D / 16];
+  float m_ref;
+  float l[3];
+};
+
+// One 32-key tile for one wavefront: scores, masks, softmax, PV products.
+// PBIG: a frame holds at least 32 tokens, so a lane's keys (a span of 20) cross at most one
 // frame boundary and their in-frame positions follow from one division per tile.
-//
-// The two wavefronts of a (query half, key half) pair -- dhalf 0 and 1, which own the two
-// halves of the head dim of the outputs -- compute the same scores but split the softmax: each
-// turns its 16 of the 32 keys into P (three states) and hands its bf16 P^T to the other
-// through LDS.  The exchange crosses the workgroup barrier at the end of the tile, so the PV
-// products of tile t run in step t+1; V is triple-buffered for that.  Both compute the
-// (cheap) row max of all 32 keys, so they agree on every rescale.
 template <int D, bool PBIG>
-__global__ __launch_bounds__(NT, 1) void profile_partial_kernel(ProfileArgs a) {
-  constexpr int KS = PLds<D>::KS;
-  constexpr int VS = PLds<D>::VS;
-  constexpr int NDBW = D / 64;     // 32-wide d blocks of the output per wavefront
-  constexpr int NKS = D / 16;
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2][TILE * KS];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[3][TILE * VS];
-  __shared__ __attribute__((aligned(16))) bf16 Qs[QG * KS];   // the 64 sampled rows
-  __shared__ __attribute__((aligned(16))) bf16x8 Px[2][NT / 64][3][64];   // P^T exchange
+__device__ __forceinline__ void profile_tile(PState<D>& st, const bf16x8 (&qf)[D / 32], const char* kt, const bf16* vt,
+                                             int32_t k0, int32_t ke, float c, uint32_t sp_lo, uint32_t sp_span,
+                                             int32_t pq, const ProfileArgs& a, int lane) {
+  using T = PTile<D>;
+  constexpr int NKS = D / 32;
+  constexpr int NDB = D / 16;
+  const int g = lane >> 4, i16 = lane & 15;
+
+  // ---- S^T = K Q^T: two 16-key blocks ----
+  f32x4 sacc[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int r = 16 * kb + i16;
+      const bf16x8 ak = *reinterpret_cast<const bf16x8*>(kt + r * T::ROW_BYTES + 16 * ((4 * ks + g) ^ T::swz_k(r)));
+      sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, qf[ks], sacc[kb], 0, 0, 0);
+    }
+
+  // ---- keys past the split's end (last tile only) do not exist ----
+  const int32_t kl = k0 + 4 * g;                // key of element (kb, r): kl + 16 kb + r
+  if (k0 + TILE > ke) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (kl + 16 * kb + r >= ke) sacc[kb][r] = -INFINITY;
+  }
+
+  // ---- shared reference max with lazy rescaling of all three states ----
+  float mx = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
+                   fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
+  mx = max_x32(max_x16(mx)) * c;
+  const bool bump = mx > st.m_ref + RESCALE_SLACK;
+  if (__any(bump)) {
+    const float m_new = bump ? mx : st.m_ref;
+    const float alpha = (st.m_ref == -INFINITY) ? 0.f : exp2f(st.m_ref - m_new);
+#pragma unroll
+    for (int x = 0; x < 3; ++x) {
+      st.l[x] *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) st.o[x][db] *= alpha;
+    }
+    st.m_ref = m_new;
+  }
+  const float m_use = (st.m_ref == -INFINITY) ? 0.f : st.m_ref;
+
+  // ---- P of the three states; masks as unsigned range tests: spatial key - sp_lo < span
+  // (frame-major keys), temporal |p_key - p_query| <= w_p on in-frame positions ----
+  const uint32_t tp_span = (uint32_t)(2 * a.w_p);
+  const int32_t pbase = PBIG ? (int32_t)fmod_((uint32_t)kl, a.divP) : 0;
+  bf16x8 pb[3];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int32_t dk = 16 * kb + r;
+      int32_t pk;
+      if constexpr (PBIG) {
+        pk = pbase + dk;
+        pk -= (pk >= a.P) ? a.P : 0;
+      } else {
+        pk = (int32_t)fmod_((uint32_t)(kl + dk), a.divP);
+      }
+      const bool in_sp = (uint32_t)(kl + dk) - sp_lo < sp_span;
+      const bool in_tp = (uint32_t)(pk - pq + a.w_p) <= tp_span;
+      const float pr = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], c, -m_use));
+      const float ps = in_sp ? pr : 0.f;
+      const float pt = in_tp ? pr : 0.f;
+      st.l[0] += pr;
+      st.l[1] += ps;
+      st.l[2] += pt;
+      pb[0][4 * kb + r] = (bf16)pr;
+      pb[1][4 * kb + r] = (bf16)ps;
+      pb[2][4 * kb + r] = (bf16)pt;
+    }
+
+  // ---- O_x^T += V^T P_x^T.  The transpose read hands lane i of each 16-lane group column i
+  // of the 4 rows x 16 columns its group addressed: group g reads keys 4g..4g+3 (and, 16 rows
+  // further, 16+4g..16+4g+3), the keys whose scores lane l holds in sacc[0] and sacc[1]. ----
+  const int vr = 4 * g + (i16 >> 2);
+  const int vc = 4 * (i16 & 3);                 // column inside the 16-channel block
+  const char* v0 = reinterpret_cast<const char*>(vt) + vr * T::ROW_BYTES;
+  const char* v1 = v0 + 16 * T::ROW_BYTES;
+  const int sw0 = T::swz_v(vr), sw1 = T::swz_v(vr + 16);
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int col = 16 * db + vc;
+    const int cb = 2 * (col & 7);
+    const i16x4 lo = lds_read_tr(reinterpret_cast<const bf16*>(v0 + 16 * ((col >> 3) ^ sw0) + cb));
+    const i16x4 hi = lds_read_tr(reinterpret_cast<const bf16*>(v1 + 16 * ((col >> 3) ^ sw1) + cb));
+    const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+    for (int x = 0; x < 3; ++x) st.o[x][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[x], st.o[x][db], 0, 0, 0);
+  }
+}
+
+template <int D, bool PBIG>
+__global__ __launch_bounds__(NT, 2) void profile_partial_kernel(ProfileArgs a) {
+  using T = PTile<D>;
+  constexpr int NKS = D / 32;
+  constexpr int NDB = D / 16;
+  __shared__ __attribute__((aligned(1024))) bf16 K0[TILE * D];
+  __shared__ __attribute__((aligned(1024))) bf16 K1[TILE * D];
+  __shared__ __attribute__((aligned(1024))) bf16 K2[TILE * D];
+  __shared__ __attribute__((aligned(1024))) bf16 K3[TILE * D];
+  __shared__ __attribute__((aligned(1024))) bf16 V0[TILE * D];
+  __shared__ __attribute__((aligned(1024))) bf16 V1[TILE * D];
+  __shared__ __attribute__((aligned(1024))) bf16 V2[TILE * D];
+  __shared__ __attribute__((aligned(1024))) bf16 V3[TILE * D];
 
   int32_t bid = blockIdx.x;
   const int32_t zq = bid % a.n_zq;
@@ -111,186 +245,96 @@ __global__ __launch_bounds__(NT, 1) void profile_partial_kernel(ProfileArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, hh = lane >> 5;
-  const int qsub = wave & 1, kp = (wave >> 1) & 1, dhalf = wave >> 2;
-  const int partner = wave ^ 4;
+  const int g = lane >> 4, i16 = lane & 15;
 
   const size_t off = (size_t)bh * (size_t)a.S * D;
   const bf16* __restrict__ Q = a.q + off;
   const bf16* __restrict__ K = a.k + off;
   const bf16* __restrict__ V = a.v + off;
 
-  const int32_t qi = zq * QG + qsub * 32 + l32;
+  const int32_t ks = split * a.keys_per_split;
+  const int32_t ke = min(a.S, ks + a.keys_per_split);
+  const int32_t ntiles = (ke - ks + TILE - 1) / TILE;
+
+  // this lane's query: q = l%16 of the wavefront's 16
+  const int32_t qi = zq * QG + wave * 16 + i16;
   int32_t tq = a.idx[min(qi, a.n_q - 1)];
   tq = min(max(tq, 0), a.S - 1);
   const int32_t fq = (int32_t)fdiv((uint32_t)tq, a.divP);
   const int32_t pq = tq - fq * a.P;
   const int32_t sp_lo = max(0, fq - a.w_f) * a.P;
   const int32_t sp_hi = min(a.F, fq + a.w_f + 1) * a.P;
+  bf16x8 qf[NKS];
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(Q + (size_t)tq * D + 32 * s + 8 * g);
 
-  // stage the sampled query rows once: wavefronts with kp == 0 and dhalf == 0 copy their rows
-  if (kp == 0 && dhalf == 0) {
-#pragma unroll
-    for (int s = 0; s < NKS; ++s)
-      *reinterpret_cast<bf16x8*>(&Qs[(qsub * 32 + l32) * KS + 16 * s + 8 * hh]) =
-          *reinterpret_cast<const bf16x8*>(Q + (size_t)tq * D + 16 * s + 8 * hh);
-  }
+  // copies of the first NBUF-1 tiles (after the query loads, which therefore retire first)
+  __builtin_amdgcn_sched_barrier(0);
+  tile_copy<D>(K, ks, a.S, K0, wave, lane, false);
+  tile_copy<D>(V, ks, a.S, V0, wave, lane, true);
+  tile_copy<D>(K, ks + TILE, a.S, K1, wave, lane, false);
+  tile_copy<D>(V, ks + TILE, a.S, V1, wave, lane, true);
+  tile_copy<D>(K, ks + 2 * TILE, a.S, K2, wave, lane, false);
+  tile_copy<D>(V, ks + 2 * TILE, a.S, V2, wave, lane, true);
 
-  const int32_t ks = split * a.keys_per_split;
-  const int32_t ke = min(a.S, ks + a.keys_per_split);
-  const int32_t ntiles = (ke - ks + TILE - 1) / TILE;
-
-  // two register stages: tile t+2 is fetched while tile t is computed and tile t+1 waits in
-  // registers for its LDS buffer, so two tiles per workgroup are in flight from HBM
-  TileStager<D, TILE, NT> stage_a, stage_b;
-  SoftmaxState<NDBW> st[3];
-  float m_ref = -INFINITY;     // reference max (log2 units) shared by the three states
-  float l[3] = {0.f, 0.f, 0.f};   // this wavefront's half of the row sums
-#pragma unroll
-  for (int x = 0; x < 3; ++x)
-#pragma unroll
-    for (int j = 0; j < NDBW; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st[x].o[j][r] = 0.f;
-  bf16x8 pown[3];              // this wavefront's P^T of the previous tile
-  const float c = a.scale * 1.44269504088896340736f;
-  const int tg = lane >> 4, ti = lane & 15;
-  const int v_row = 4 * (tg >> 1) + (ti >> 2);
-  const int v_col = 16 * (tg & 1) + 4 * (ti & 3) + dhalf * (D / 2);
-
-  if (ntiles > 0) {
-    stage_a.load(K, V, ks, a.S, tid);
-    stage_a.template store<KS, VS>(Ks[0], Vs[0], tid);
-  }
-  // Fetches are unconditional (past the last tile they repeat it, and nothing stores that copy):
-  // a conditional fetch would make the compiler wait for every load in flight before storing
-  // the older stage.
-  const int32_t t_last = max(ntiles - 1, 0);
-  stage_b.load(K, V, ks + min(1, t_last) * TILE, a.S, tid);
-  __syncthreads();
-  // step t: fetch tile t+2 into `fetch`, compute, then move tile t+1 from `ready` into LDS
-  auto step = [&](int32_t t, TileStager<D, TILE, NT>& fetch, TileStager<D, TILE, NT>& ready) {
-    fetch.load(K, V, ks + min(t + 2, t_last) * TILE, a.S, tid);
-
-    // ---- PV of tile t-1: own P^T for key step dhalf, the partner's for the other ----
-    if (t >= 1) {
-      bf16x8 pq3[3];
-#pragma unroll
-      for (int x = 0; x < 3; ++x) pq3[x] = Px[(t - 1) & 1][partner][x][lane];
-      const bf16* vt = Vs[(t - 1) % 3];
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const bf16* vb = &vt[(kp * 32 + 16 * s + v_row) * VS + v_col];
-        const bool mine = s == dhalf;
-#pragma unroll
-        for (int j = 0; j < NDBW; ++j) {
-          const bf16x8 av = load_vt(vb + j * 32, VS);
-#pragma unroll
-          for (int x = 0; x < 3; ++x)
-            st[x].o[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, mine ? pown[x] : pq3[x], st[x].o[j], 0, 0, 0);
-        }
-      }
-    }
-
-    if (t < ntiles) {
-      const int buf = t & 1;
-      f32x16 sacc;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
-#pragma unroll
-      for (int s = 0; s < NKS; ++s) {
-        const bf16x8 ak = *reinterpret_cast<const bf16x8*>(&Ks[buf][(kp * 32 + l32) * KS + 16 * s + 8 * hh]);
-        const bf16x8 bq = *reinterpret_cast<const bf16x8*>(&Qs[(qsub * 32 + l32) * KS + 16 * s + 8 * hh]);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, bq, sacc, 0, 0, 0);
-      }
-      const int32_t kbase = ks + t * TILE + kp * 32 + 4 * hh;
-      // keys past the split's end (last tile only) do not exist
-      if (ks + (t + 1) * TILE > ke) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (kbase + 8 * (r >> 2) + (r & 3) >= ke) sacc[r] = -INFINITY;
-      }
-      // shared reference max (over all 32 keys, in both wavefronts of the pair) with lazy
-      // rescaling of all three states; the accumulators hold the products up to tile t-1
-      float mx = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
-      const bool bump = mx > m_ref + RESCALE_SLACK;
-      if (__any(bump)) {
-        const float m_new = bump ? mx : m_ref;
-        const float alpha = (m_ref == -INFINITY) ? 0.f : exp2f(m_ref - m_new);
-#pragma unroll
-        for (int x = 0; x < 3; ++x) {
-          l[x] *= alpha;
-#pragma unroll
-          for (int j = 0; j < NDBW; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) st[x].o[j][r] *= alpha;
-        }
-        m_ref = m_new;
-      }
-      const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-      // masks as unsigned range tests: spatial key - sp_lo < sp_hi - sp_lo (frame-major keys),
-      // temporal |p_key - p_query| <= w_p on in-frame positions
-      const uint32_t sp_base = (uint32_t)(kbase - sp_lo), sp_span = (uint32_t)(sp_hi - sp_lo);
-      const int32_t pbase = PBIG ? (int32_t)fmod_((uint32_t)kbase, a.divP) : 0;
-      if (dhalf == 0)
-        half_softmax<0, PBIG>(sacc, c, m_use, kbase, sp_base, sp_span, pbase, pq, a, l, pown);
-      else
-        half_softmax<1, PBIG>(sacc, c, m_use, kbase, sp_base, sp_span, pbase, pq, a, l, pown);
-#pragma unroll
-      for (int x = 0; x < 3; ++x) Px[t & 1][wave][x][lane] = pown[x];
-    }
-    if (t + 1 < ntiles) ready.template store<KS, VS>(Ks[(t + 1) & 1], Vs[(t + 1) % 3], tid);
-    __syncthreads();
-  };
-  for (int32_t t = 0; t <= ntiles; t += 2) {
-    step(t, stage_a, stage_b);
-    if (t + 1 > ntiles) break;
-    step(t + 1, stage_b, stage_a);
-  }
-
-  // ---- row sums of the pair, then this wavefront's partial states (its half of the head dim)
-  float* lx = reinterpret_cast<float*>(&Px[0][0][0][0]);     // reused: [NT / 64][3][64]
-#pragma unroll
-  for (int x = 0; x < 3; ++x) lx[(wave * 3 + x) * 64 + lane] = l[x];
-  __syncthreads();
-#pragma unroll
-  for (int x = 0; x < 3; ++x) l[x] += lx[(partner * 3 + x) * 64 + lane];
-  const int32_t nparts = 2 * a.nsplit;
-  const int32_t part = split * 2 + kp;
-  const int32_t qpad = a.n_zq * QG;
-  const int32_t qloc = zq * QG + qsub * 32 + l32;
+  PState<D> st;
 #pragma unroll
   for (int x = 0; x < 3; ++x) {
-    const float l_tot = l[x] + __shfl_xor(l[x], 32, 64);
-    const size_t slot = (((size_t)bh * nparts + part) * 3 + x) * qpad + qloc;
-    if (hh == 0 && dhalf == 0) {
-      a.part_ml[slot * 2 + 0] = m_ref;
+    st.l[x] = 0.f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) st.o[x][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  st.m_ref = -INFINITY;
+  const float c = a.scale * 1.44269504088896340736f;
+
+  // tile t: its copies (issued NBUF-1 tiles earlier) retire, the barrier publishes them and
+  // frees the buffer of tile t-1, which receives tile t+NBUF-1.  Copies past the last tile
+  // repeat rows of the sequence into buffers no later tile reads.
+  auto step = [&](int32_t t, const bf16* kt, const bf16* vt, bf16* kn, bf16* vn) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm((NBUF - 2) * T::CPW, 0));
+    tile_barrier();
+    tile_copy<D>(K, ks + (t + NBUF - 1) * TILE, a.S, kn, wave, lane, false);
+    tile_copy<D>(V, ks + (t + NBUF - 1) * TILE, a.S, vn, wave, lane, true);
+    profile_tile<D, PBIG>(st, qf, reinterpret_cast<const char*>(kt), vt, ks + t * TILE, ke, c, (uint32_t)sp_lo,
+                          (uint32_t)(sp_hi - sp_lo), pq, a, lane);
+  };
+  for (int32_t t = 0; t < ntiles; t += NBUF) {
+    step(t, K0, V0, K3, V3);
+    if (t + 1 >= ntiles) break;
+    step(t + 1, K1, V1, K0, V0);
+    if (t + 2 >= ntiles) break;
+    step(t + 2, K2, V2, K1, V1);
+    if (t + 3 >= ntiles) break;
+    step(t + 3, K3, V3, K2, V2);
+  }
+  __builtin_amdgcn_s_waitcnt(VMCNT0);
+
+  // ---- this wavefront's partial states: row sums over the four lane groups ----
+  const int32_t qpad = a.n_zq * QG;
+  const int32_t qloc = zq * QG + wave * 16 + i16;
+#pragma unroll
+  for (int x = 0; x < 3; ++x) {
+    const float l_tot = sum_x32(sum_x16(st.l[x]));
+    const size_t slot = (((size_t)bh * a.nsplit + split) * 3 + x) * qpad + qloc;
+    if (g == 0) {
+      a.part_ml[slot * 2 + 0] = st.m_ref;
       a.part_ml[slot * 2 + 1] = l_tot;
     }
-    float* po = a.part_o + slot * D + dhalf * (D / 2);
+    // lane l holds channels 16 db + 4 g + r of its query
+    float* po = a.part_o + slot * D + 4 * g;
 #pragma unroll
-    for (int j = 0; j < NDBW; ++j)
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        f32x4 v4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = st[x].o[j][4 * rq + e];
-        *reinterpret_cast<f32x4*>(po + 32 * j + 8 * rq + 4 * hh) = v4;
-      }
+    for (int db = 0; db < NDB; ++db) *reinterpret_cast<f32x4*>(po + 16 * db) = st.o[x][db];
   }
 }
 
 template <int D>
 __global__ __launch_bounds__(D) void profile_merge_kernel(ProfileArgs a) {
-  __shared__ float sm[3][2 * MAX_SPLIT], sl[3][2 * MAX_SPLIT], wt[3][2 * MAX_SPLIT];
+  __shared__ float sm[3][MAX_SPLIT], sl[3][MAX_SPLIT], wt[3][MAX_SPLIT];
   __shared__ double red[2][D];
   const int32_t bh = blockIdx.x / a.n_q;
   const int32_t qg = blockIdx.x - bh * a.n_q;
   const int tid = threadIdx.x;
-  const int32_t nparts = 2 * a.nsplit;
+  const int32_t nparts = a.nsplit;
   const int32_t qpad = a.n_zq * QG;
   for (int t = tid; t < 3 * nparts; t += D) {
     const int x = t / nparts, p = t - (t / nparts) * nparts;
@@ -374,7 +418,7 @@ __global__ __launch_bounds__(NT_RED) void profile_finish_kernel(ProfileArgs a) {
 ProfilePlan profile_plan(int32_t BH, int32_t S, int32_t D, int32_t n_q) {
   ProfilePlan p;
   p.n_zq = (n_q + QG - 1) / QG;
-  // as many key splits as fit TARGET_WGS workgroups (two per CU) without a partial round
+  // as many key splits as fit TARGET_WGS workgroups (two per CU) in one round
   int64_t want = TARGET_WGS / ((int64_t)BH * p.n_zq);
   const int64_t max_tiles = (S + TILE - 1) / TILE;
   if (want > MAX_SPLIT) want = MAX_SPLIT;
@@ -383,7 +427,7 @@ ProfilePlan profile_plan(int32_t BH, int32_t S, int32_t D, int32_t n_q) {
   const int64_t per = (S + want - 1) / want;
   p.keys_per_split = (int32_t)(((per + TILE - 1) / TILE) * TILE);
   p.nsplit = (int32_t)((S + p.keys_per_split - 1) / p.keys_per_split);
-  const size_t slots = (size_t)BH * (2 * p.nsplit) * 3 * (size_t)(p.n_zq * QG);
+  const size_t slots = (size_t)BH * p.nsplit * 3 * (size_t)(p.n_zq * QG);
   p.ml_floats = slots * 2;
   p.o_floats = slots * (size_t)D;
   p.sq_doubles = (size_t)BH * n_q * 2;

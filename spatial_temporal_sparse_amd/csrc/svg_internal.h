@@ -73,55 +73,11 @@ __device__ __forceinline__ void band_interval(const Band& b, int32_t r, int32_t&
 }
 
 // ------------------------------------------------------------------------------------------
-// LDS staging helpers shared by the attention and profiling kernels.
+// LDS transpose read (ds_read_b64_tr_b16) used by the attention and profiling kernels.
 // ------------------------------------------------------------------------------------------
 __device__ __forceinline__ i16x4 lds_read_tr(const bf16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
 }
-
-// A operand of one O^T += V^T P^T MFMA (v_mfma_f32_32x32x16_bf16) from a row-major [key][d]
-// V tile in LDS.  The 64-bit transpose read hands lane j of each 16-lane group column j%4 of
-// the rows its group addressed; with the per-lane address p = &V[key0 + 4*h + (i>>2)][d0 +
-// 16*(g&1) + 4*(i&3)] (g = lane/16, h = g/2, i = lane%16) lane l receives V[key0 + 4h + e][d0
-// + l%32] for e = 0..3, and the second read (8 rows further) keys +8..+11.
-__device__ __forceinline__ bf16x8 load_vt(const bf16* p, int row_stride) {
-  const i16x4 lo = lds_read_tr(p);
-  const i16x4 hi = lds_read_tr(p + 8 * row_stride);
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
-// Global -> register staging of a ROWS x D tile starting at row k0 (rows clamped to S-1),
-// and register -> LDS store with row strides KS / VS, for an NTH-thread workgroup.
-template <int D, int ROWS, int NTH>
-struct TileStager {
-  static constexpr int CPR = D / 8;                 // 16-byte chunks per row
-  static constexpr int CHUNKS = ROWS * CPR / NTH;   // per thread per tensor
-  u32x4 k[CHUNKS], v[CHUNKS];
-
-  __device__ __forceinline__ void load(const bf16* __restrict__ K, const bf16* __restrict__ V, int32_t k0, int32_t S,
-                                       int tid) {
-#pragma unroll
-    for (int i = 0; i < CHUNKS; ++i) {
-      const int c = tid + i * NTH;
-      const int row = c / CPR;
-      const int col = (c % CPR) * 8;
-      const size_t grow = (size_t)min(k0 + row, S - 1);
-      k[i] = *reinterpret_cast<const u32x4*>(K + grow * D + col);
-      v[i] = *reinterpret_cast<const u32x4*>(V + grow * D + col);
-    }
-  }
-  template <int KS, int VS>
-  __device__ __forceinline__ void store(bf16* ks, bf16* vs, int tid) const {
-#pragma unroll
-    for (int i = 0; i < CHUNKS; ++i) {
-      const int c = tid + i * NTH;
-      const int row = c / CPR;
-      const int col = (c % CPR) * 8;
-      *reinterpret_cast<u32x4*>(ks + row * KS + col) = k[i];
-      *reinterpret_cast<u32x4*>(vs + row * VS + col) = v[i];
-    }
-  }
-};
 
 // ------------------------------------------------------------------------------------------
 // Launchers (one per kernel family); each returns hipGetLastError() after enqueueing.
@@ -180,8 +136,8 @@ struct ProfileArgs {
   FastDiv divP;
   float scale;
   int32_t nsplit, keys_per_split;
-  float* part_ml;             // [BH][2*nsplit][3][n_zq*64][2]
-  float* part_o;              // [BH][2*nsplit][3][n_zq*64][D]
+  float* part_ml;             // [BH][nsplit][3][n_zq*64][2]
+  float* part_o;              // [BH][nsplit][3][n_zq*64][D]
   double* row_sq;             // [BH][n_q][2] squared errors of each sampled row
   float* mse;                 // [BH][2]
   uint8_t* kind;              // [BH]

@@ -71,6 +71,17 @@ def test_profile_planted_cogvideox_shape(gpu):
     _check_profile(gpu, q, k, v, idx, g, wl.w_f, wl.w_p, expect=expected_planted_kinds(wl), what="cogvideox")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_profile_small_frames(gpu, D):
+    # frames of 24 tokens (fewer than 32: in-frame positions per key, not per tile), 64 heads so
+    # that each key split holds 6 tiles of 32 keys (the tile buffers rotate), ragged last split
+    g = Geometry(1, 64, 60, 4, 6, D)
+    note(f"profile small frames D={D}")
+    q, k, v = make_qkv(Workload("smallp", g, 1, 5, 64, 33, 133, planted=True), device=DEV)
+    idx = sample_queries(g.S, 64, 133)
+    _check_profile(gpu, q, k, v, idx, g, 1, 5, what=f"small frames D={D}")
+
+
 def test_profile_full_cover_choice(gpu):
     g = Geometry(1, 2, 4, 6, 6, 128)
     note("profile with a spatial window covering every frame")
