@@ -104,6 +104,7 @@ svg_status svg_qknorm_rope(const void* q, const void* k, void* q_out, void* k_ou
  * mse_out:   fp32 [B*H][2] device array (spatial, temporal).
  * kind_out:  uint8 [B*H] device array.
  * ws:        >= svg_workspace_bytes(SVG_OP_PROFILE, &g, n_q) bytes of device memory.
+ * One head of K or V must stay under 4 GB (S * D * 2 bytes), else SVG_ERR_UNSUPPORTED.
  */
 svg_status svg_profile_heads(const void* q, const void* k, const void* v, const int32_t* q_idx, int32_t n_q,
                              svg_geom g, svg_windows w, float scale, float* mse_out, uint8_t* kind_out,

@@ -119,6 +119,14 @@ SVG_API svg_status svg_qknorm_rope(const void* q, const void* k, void* q_out, vo
   return hip_status(svg::launch_qknorm_rope(a, (hipStream_t)stream), "svg_qknorm_rope");
 }
 
+// The attention and profiling kernels address a head's rows with 32-bit byte offsets.
+static svg_status check_head_bytes(const svg_geom& g) {
+  const int64_t S = (int64_t)g.F * g.HH * g.WW;
+  if (S * g.D * 2 >= ((int64_t)1 << 32))
+    return fail(SVG_ERR_UNSUPPORTED, "one head of S=%lld rows x D=%d exceeds 4 GB", (long long)S, g.D);
+  return SVG_OK;
+}
+
 SVG_API svg_status svg_profile_heads(const void* q, const void* k, const void* v, const int32_t* q_idx, int32_t n_q,
                                      svg_geom g, svg_windows w, float scale, float* mse_out, uint8_t* kind_out,
                                      void* ws, size_t ws_bytes, void* stream) {
@@ -126,6 +134,7 @@ SVG_API svg_status svg_profile_heads(const void* q, const void* k, const void* v
   if ((s = check_geom(g, true)) != SVG_OK) return s;
   if ((s = check_windows(w)) != SVG_OK) return s;
   if ((s = check_ptrs({{q, "q"}, {k, "k"}, {v, "v"}})) != SVG_OK) return s;
+  if ((s = check_head_bytes(g)) != SVG_OK) return s;
   if (q_idx == nullptr || mse_out == nullptr || kind_out == nullptr)
     return fail(SVG_ERR_INVALID, "q_idx, mse_out and kind_out must not be NULL");
   if (((uintptr_t)q_idx & 3u) || ((uintptr_t)mse_out & 3u))
@@ -227,14 +236,6 @@ SVG_API svg_status svg_build_block_mask(const uint8_t* kind, svg_geom g, svg_win
   a.divP = svg::make_fastdiv((uint32_t)a.P);
   a.divF = svg::make_fastdiv((uint32_t)g.F);
   return hip_status(svg::launch_block_mask(a, (hipStream_t)stream), "svg_build_block_mask");
-}
-
-// The attention kernel addresses a head's rows with 32-bit byte offsets.
-static svg_status check_head_bytes(const svg_geom& g) {
-  const int64_t S = (int64_t)g.F * g.HH * g.WW;
-  if (S * g.D * 2 >= ((int64_t)1 << 32))
-    return fail(SVG_ERR_UNSUPPORTED, "one head of S=%lld rows x D=%d exceeds 4 GB", (long long)S, g.D);
-  return SVG_OK;
 }
 
 static void fill_attn(svg::AttnArgs& a, svg_geom g, svg_windows w, float scale) {

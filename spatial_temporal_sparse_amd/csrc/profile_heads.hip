@@ -120,12 +120,30 @@ struct PState {
   float l[3];
 };
 
+// sum of the eight bf16 values of p added to acc (v_dot2_f32_bf16 against (1, 1))
+__device__ __forceinline__ float add_bf16x8(const bf16x8& p, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 4, 5), one, acc, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 6, 7), one, acc, false);
+}
+
+// Temporal-mask modes.  A lane's keys in a tile are kl + dk, dk in {0..3, 16..19}.
+//   TP_INTERVAL: frames of >= 32 tokens (the lane's keys cross at most one frame boundary) and
+//     a band that leaves >= 20 positions of a frame out (P - 2 w_p - 1 >= 20).  The keys of the
+//     band in the first frame, [lo0, hi0] in dk, and in the next, [lo0 + P, hi0 + P], are then
+//     at least 20 apart, so at most one of them meets the lane's keys: one interval [a, b) of
+//     dk per tile, clipped at the frame boundary.
+//   TP_PER_KEY: in-frame position of every key by one division.
+constexpr int TP_PER_KEY = 0;
+constexpr int TP_INTERVAL = 1;
+
 // One 32-key tile for one wavefront: scores, masks, softmax, PV products.
-// PBIG: a frame holds at least 32 tokens, so a lane's keys (a span of 20) cross at most one
-// frame boundary and their in-frame positions follow from one division per tile.
-template <int D, bool PBIG>
+template <int D, int TPM>
 __device__ __forceinline__ void profile_tile(PState<D>& st, const bf16x8 (&qf)[D / 32], const char* kt, const bf16* vt,
-                                             int32_t k0, int32_t ke, float c, uint32_t sp_lo, uint32_t sp_span,
+                                             int32_t k0, int32_t ke, float c, int32_t sp_lo, uint32_t sp_span,
                                              int32_t pq, const ProfileArgs& a, int lane) {
   using T = PTile<D>;
   constexpr int NKS = D / 32;
@@ -156,8 +174,11 @@ __device__ __forceinline__ void profile_tile(PState<D>& st, const bf16x8 (&qf)[D
   }
 
   // ---- shared reference max with lazy rescaling of all three states ----
-  float mx = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
-                   fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[kb][r]);
   mx = max_x32(max_x16(mx)) * c;
   const bool bump = mx > st.m_ref + RESCALE_SLACK;
   if (__any(bump)) {
@@ -173,35 +194,42 @@ __device__ __forceinline__ void profile_tile(PState<D>& st, const bf16x8 (&qf)[D
   }
   const float m_use = (st.m_ref == -INFINITY) ? 0.f : st.m_ref;
 
-  // ---- P of the three states; masks as unsigned range tests: spatial key - sp_lo < span
-  // (frame-major keys), temporal |p_key - p_query| <= w_p on in-frame positions ----
-  const uint32_t tp_span = (uint32_t)(2 * a.w_p);
-  const int32_t pbase = PBIG ? (int32_t)fmod_((uint32_t)kl, a.divP) : 0;
+  // ---- masks as unsigned range tests on dk: spatial keys [sp_lo, sp_lo + sp_span) (frame-major),
+  // temporal keys within w_p of the query's in-frame position, in the same frame ----
+  const int32_t sp_a = sp_lo - kl;
+  int32_t tp_a = 0;
+  uint32_t tp_span = 0;
+  if constexpr (TPM == TP_INTERVAL) {
+    const int32_t pbase = (int32_t)fmod_((uint32_t)kl, a.divP);
+    const int32_t wth = a.P - pbase;             // dk >= wth: next frame
+    const int32_t lo0 = pq - a.w_p - pbase, hi0 = lo0 + 2 * a.w_p;
+    const bool first = hi0 >= 0;
+    tp_a = first ? max(lo0, 0) : max(lo0 + a.P, wth);
+    const int32_t tp_b = first ? min(hi0 + 1, wth) : hi0 + a.P + 1;
+    tp_span = (uint32_t)max(tp_b - tp_a, 0);
+  }
   bf16x8 pb[3];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int32_t dk = 16 * kb + r;
-      int32_t pk;
-      if constexpr (PBIG) {
-        pk = pbase + dk;
-        pk -= (pk >= a.P) ? a.P : 0;
+      bool in_tp;
+      if constexpr (TPM == TP_INTERVAL) {
+        in_tp = (uint32_t)(dk - tp_a) < tp_span;
       } else {
-        pk = (int32_t)fmod_((uint32_t)(kl + dk), a.divP);
+        const int32_t pk = (int32_t)fmod_((uint32_t)(kl + dk), a.divP);
+        in_tp = (uint32_t)(pk - pq + a.w_p) <= (uint32_t)(2 * a.w_p);
       }
-      const bool in_sp = (uint32_t)(kl + dk) - sp_lo < sp_span;
-      const bool in_tp = (uint32_t)(pk - pq + a.w_p) <= tp_span;
+      const bool in_sp = (uint32_t)(dk - sp_a) < sp_span;
       const float pr = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], c, -m_use));
-      const float ps = in_sp ? pr : 0.f;
-      const float pt = in_tp ? pr : 0.f;
-      st.l[0] += pr;
-      st.l[1] += ps;
-      st.l[2] += pt;
       pb[0][4 * kb + r] = (bf16)pr;
-      pb[1][4 * kb + r] = (bf16)ps;
-      pb[2][4 * kb + r] = (bf16)pt;
+      pb[1][4 * kb + r] = (bf16)(in_sp ? pr : 0.f);
+      pb[2][4 * kb + r] = (bf16)(in_tp ? pr : 0.f);
     }
+  // row sums of the bf16 weights the PV products use
+#pragma unroll
+  for (int x = 0; x < 3; ++x) st.l[x] = add_bf16x8(pb[x], st.l[x]);
 
   // ---- O_x^T += V^T P_x^T.  The transpose read hands lane i of each 16-lane group column i
   // of the 4 rows x 16 columns its group addressed: group g reads keys 4g..4g+3 (and, 16 rows
@@ -223,7 +251,7 @@ __device__ __forceinline__ void profile_tile(PState<D>& st, const bf16x8 (&qf)[D
   }
 }
 
-template <int D, bool PBIG>
+template <int D, int TPM>
 __global__ __launch_bounds__(NT, 2) void profile_partial_kernel(ProfileArgs a) {
   using T = PTile<D>;
   constexpr int NKS = D / 32;
@@ -295,8 +323,8 @@ __global__ __launch_bounds__(NT, 2) void profile_partial_kernel(ProfileArgs a) {
     tile_barrier();
     tile_copy<D>(K, ks + (t + NBUF - 1) * TILE, a.S, kn, wave, lane, false);
     tile_copy<D>(V, ks + (t + NBUF - 1) * TILE, a.S, vn, wave, lane, true);
-    profile_tile<D, PBIG>(st, qf, reinterpret_cast<const char*>(kt), vt, ks + t * TILE, ke, c, (uint32_t)sp_lo,
-                          (uint32_t)(sp_hi - sp_lo), pq, a, lane);
+    profile_tile<D, TPM>(st, qf, reinterpret_cast<const char*>(kt), vt, ks + t * TILE, ke, c, sp_lo,
+                         (uint32_t)(sp_hi - sp_lo), pq, a, lane);
   };
   for (int32_t t = 0; t < ntiles; t += NBUF) {
     step(t, K0, V0, K3, V3);
@@ -326,6 +354,13 @@ __global__ __launch_bounds__(NT, 2) void profile_partial_kernel(ProfileArgs a) {
     for (int db = 0; db < NDB; ++db) *reinterpret_cast<f32x4*>(po + 16 * db) = st.o[x][db];
   }
 }
+
+// Explicit instantiations: without them the host pass emitted the launch stub of only one of
+// the two kernels that the launcher chooses between.
+template __global__ void profile_partial_kernel<128, TP_PER_KEY>(ProfileArgs);
+template __global__ void profile_partial_kernel<128, TP_INTERVAL>(ProfileArgs);
+template __global__ void profile_partial_kernel<64, TP_PER_KEY>(ProfileArgs);
+template __global__ void profile_partial_kernel<64, TP_INTERVAL>(ProfileArgs);
 
 template <int D>
 __global__ __launch_bounds__(D) void profile_merge_kernel(ProfileArgs a) {
@@ -438,14 +473,15 @@ hipError_t launch_profile(const ProfileArgs& a, hipStream_t st) {
   const dim3 g1((unsigned)((int64_t)a.BH * a.nsplit * a.n_zq));
   const dim3 g2((unsigned)((int64_t)a.BH * a.n_q));
   const dim3 g3((unsigned)a.BH);
-  const bool pbig = a.P >= 32;
+  // the band test per tile needs frames of >= 32 tokens and >= 20 positions outside the band
+  const bool interval = a.P >= 32 && (int64_t)a.P - 2 * (int64_t)a.w_p - 1 >= 20;
   if (a.D == 128) {
-    if (pbig) profile_partial_kernel<128, true><<<g1, NT, 0, st>>>(a);
-    else profile_partial_kernel<128, false><<<g1, NT, 0, st>>>(a);
+    if (interval) profile_partial_kernel<128, TP_INTERVAL><<<g1, NT, 0, st>>>(a);
+    else profile_partial_kernel<128, TP_PER_KEY><<<g1, NT, 0, st>>>(a);
     profile_merge_kernel<128><<<g2, 128, 0, st>>>(a);
   } else if (a.D == 64) {
-    if (pbig) profile_partial_kernel<64, true><<<g1, NT, 0, st>>>(a);
-    else profile_partial_kernel<64, false><<<g1, NT, 0, st>>>(a);
+    if (interval) profile_partial_kernel<64, TP_INTERVAL><<<g1, NT, 0, st>>>(a);
+    else profile_partial_kernel<64, TP_PER_KEY><<<g1, NT, 0, st>>>(a);
     profile_merge_kernel<64><<<g2, 64, 0, st>>>(a);
   } else {
     return hipErrorInvalidValue;

@@ -109,6 +109,8 @@ def test_argument_checks(svg):
     assert L.svg_dense_attn(FAKE, FAKE, FAKE, big, 0.1, FAKE, None) == -2
     assert L.svg_sparse_attn(FAKE, FAKE, FAKE, None, None, None, FAKE, big, W(1, 2), 0.125, FAKE, None, FAKE,
                              1 << 20, None) == -2
+    assert L.svg_profile_heads(FAKE, FAKE, FAKE, FAKE, 64, big, W(1, 2), 0.125, FAKE, FAKE, FAKE, 1 << 20,
+                               None) == -2
     # rope slices must be even and add up to D; eps must be positive
     assert L.svg_qknorm_rope(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1e-6, 1e4, 24, 21, 19, good, None) == -1
     assert L.svg_qknorm_rope(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.0, 1e4, 24, 20, 20, good, None) == -1

@@ -71,15 +71,24 @@ def test_profile_planted_cogvideox_shape(gpu):
     _check_profile(gpu, q, k, v, idx, g, wl.w_f, wl.w_p, expect=expected_planted_kinds(wl), what="cogvideox")
 
 
-@pytest.mark.parametrize("D", [64, 128])
-def test_profile_small_frames(gpu, D):
-    # frames of 24 tokens (fewer than 32: in-frame positions per key, not per tile), 64 heads so
-    # that each key split holds 6 tiles of 32 keys (the tile buffers rotate), ragged last split
-    g = Geometry(1, 64, 60, 4, 6, D)
-    note(f"profile small frames D={D}")
-    q, k, v = make_qkv(Workload("smallp", g, 1, 5, 64, 33, 133, planted=True), device=DEV)
+# In-frame positions per key (frames of < 32 tokens, or a band leaving < 20 positions of a frame
+# out) instead of one band interval per tile.  64 heads, so that each key split holds several
+# tiles of 32 keys (the tile buffers rotate); the last split is ragged.
+PER_KEY_CASES = [
+    ("P24_D64", 4, 6, 64, 5),
+    ("P24_D128", 4, 6, 128, 5),
+    ("P36_wide_band", 6, 6, 128, 10),
+]
+
+
+@pytest.mark.parametrize("case", PER_KEY_CASES, ids=[c[0] for c in PER_KEY_CASES])
+def test_profile_per_key_positions(gpu, case):
+    _, HH, WW, D, w_p = case
+    g = Geometry(1, 64, 60, HH, WW, D)
+    note(f"profile per-key positions {case[0]}")
+    q, k, v = make_qkv(Workload("perkey", g, 1, w_p, 64, 33, 133, planted=True), device=DEV)
     idx = sample_queries(g.S, 64, 133)
-    _check_profile(gpu, q, k, v, idx, g, 1, 5, what=f"small frames D={D}")
+    _check_profile(gpu, q, k, v, idx, g, 1, w_p, what=case[0])
 
 
 def test_profile_full_cover_choice(gpu):
