@@ -9,7 +9,9 @@
 // register or LDS work.  D/8 lanes own a row (8 channels = one 16-byte vector each); the
 // sum of squares is reduced across those lanes with DPP lane permutations.  The cos/sin of
 // every (axis, position, pair) -- F*dt/2 + HH*dh/2 + WW*dw/2 entries -- are computed once
-// per block in fp64 and kept in LDS as fp32 pairs, so no transcendental runs per element.
+// per block and kept in LDS as fp32 pairs, so no transcendental runs per element: the
+// inverse frequency of each (axis, pair) in fp64, each angle in fp64 reduced to [-pi, pi],
+// its cosine and sine in fp32 (within about one fp32 ulp of the exact values).
 #include "svg_internal.h"
 
 namespace svg {
@@ -46,35 +48,7 @@ __global__ __launch_bounds__(ROPE_THREADS) void qknorm_rope_kernel(RopeArgs a) {
   constexpr int RPP = ROPE_THREADS / LPR;    // rows per pass of the block
   const int which = blockIdx.y;              // 0: Q, 1: K
   const int tid = threadIdx.x;
-
-  // ---- per-block cos/sin tables (fp64 angle and sincos, stored as fp32) ----
-  const int nt = a.dt / 2, nh = a.dh / 2, nw = a.dw / 2;
-  const int Et = a.F * nt, Eh = a.HH * nh, Ew = a.WW * nw;
-  for (int e = tid; e < Et + Eh + Ew; e += ROPE_THREADS) {
-    int pos, j, n;
-    if (e < Et) { pos = e / nt; j = e - pos * nt; n = a.dt; }
-    else if (e < Et + Eh) { const int r = e - Et; pos = r / nh; j = r - pos * nh; n = a.dh; }
-    else { const int r = e - Et - Eh; pos = r / nw; j = r - pos * nw; n = a.dw; }
-    const double theta = (double)pos * pow(a.base, -2.0 * (double)j / (double)n);
-    double s, c;
-    sincos(theta, &s, &c);
-    tab[e] = make_float2((float)c, (float)s);
-  }
-
-  // ---- this lane's four channel pairs: table base and per-position stride ----
   const int lane_c = tid % LPR;
-  int tab_base[4], tab_stride[4], axis[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int pp = lane_c * 4 + i;
-    if (pp < nt) { axis[i] = 0; tab_base[i] = pp; tab_stride[i] = nt; }
-    else if (pp < nt + nh) { axis[i] = 1; tab_base[i] = Et + (pp - nt); tab_stride[i] = nh; }
-    else { axis[i] = 2; tab_base[i] = Et + Eh + (pp - nt - nh); tab_stride[i] = nw; }
-  }
-  float w[8];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) w[c] = a.w[which][lane_c * 8 + c];
-  __syncthreads();
 
   const u32x4* __restrict__ in = reinterpret_cast<const u32x4*>(a.in[which]);
   u32x4* __restrict__ out = reinterpret_cast<u32x4*>(a.out[which]);
@@ -92,6 +66,51 @@ __global__ __launch_bounds__(ROPE_THREADS) void qknorm_rope_kernel(RopeArgs a) {
       raw[u] = in[row * LPR + lane_c];
     }
   };
+  const int64_t step = stride * ROPE_UNROLL;
+  u32x4 ra[ROPE_UNROLL], rb[ROPE_UNROLL];
+  int64_t base = (int64_t)blockIdx.x * RPP + tid / LPR;
+  // the first rows are fetched before the tables are built, so that their latency overlaps
+  load(ra, base);
+
+  // ---- per-block cos/sin tables: inverse frequencies base^(-2j/n) in fp64 (one pow per axis
+  // and pair), angles pos * freq in fp64 reduced to [-pi, pi], cos/sin in fp32 ----
+  __shared__ double invf[3 * 64];
+  const int nt = a.dt / 2, nh = a.dh / 2, nw = a.dw / 2;
+  if (tid < nt + nh + nw) {
+    int j, n;
+    if (tid < nt) { j = tid; n = a.dt; }
+    else if (tid < nt + nh) { j = tid - nt; n = a.dh; }
+    else { j = tid - nt - nh; n = a.dw; }
+    invf[tid] = pow(a.base, -2.0 * (double)j / (double)n);
+  }
+  __syncthreads();
+  const int Et = a.F * nt, Eh = a.HH * nh, Ew = a.WW * nw;
+  for (int e = tid; e < Et + Eh + Ew; e += ROPE_THREADS) {
+    int pos, f;
+    if (e < Et) { pos = e / nt; f = e - pos * nt; }
+    else if (e < Et + Eh) { const int r = e - Et; pos = r / nh; f = nt + r - pos * nh; }
+    else { const int r = e - Et - Eh; pos = r / nw; f = nt + nh + r - pos * nw; }
+    const double theta = (double)pos * invf[f];
+    const double r2 = theta - 6.283185307179586 * rint(theta * 0.15915494309189535);
+    float s, c;
+    sincosf((float)r2, &s, &c);
+    tab[e] = make_float2(c, s);
+  }
+
+  // ---- this lane's four channel pairs: table base and per-position stride ----
+  int tab_base[4], tab_stride[4], axis[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int pp = lane_c * 4 + i;
+    if (pp < nt) { axis[i] = 0; tab_base[i] = pp; tab_stride[i] = nt; }
+    else if (pp < nt + nh) { axis[i] = 1; tab_base[i] = Et + (pp - nt); tab_stride[i] = nh; }
+    else { axis[i] = 2; tab_base[i] = Et + Eh + (pp - nt - nh); tab_stride[i] = nw; }
+  }
+  float w[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) w[c] = a.w[which][lane_c * 8 + c];
+  __syncthreads();
+
   auto process = [&](const u32x4 (&raw)[ROPE_UNROLL], int64_t base) {
 #pragma unroll
     for (int u = 0; u < ROPE_UNROLL; ++u) {
@@ -131,10 +150,6 @@ __global__ __launch_bounds__(ROPE_THREADS) void qknorm_rope_kernel(RopeArgs a) {
     }
   };
 
-  const int64_t step = stride * ROPE_UNROLL;
-  u32x4 ra[ROPE_UNROLL], rb[ROPE_UNROLL];
-  int64_t base = (int64_t)blockIdx.x * RPP + tid / LPR;
-  load(ra, base);
   for (; base < total; base += 2 * step) {
     load(rb, base + step);
     process(ra, base);
