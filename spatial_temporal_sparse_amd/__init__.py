@@ -3,7 +3,7 @@
 Argument marshalling only.  Every step of the path runs in the HIP kernels of libsvg.so;
 PyTorch supplies device memory and the current HIP stream.  Importing this package loads
 the library and raises ImportError if it has not been built
-(``python -m spatial_temporal_sparse_amd.build``); there is no fallback.
+(``python spatial_temporal_sparse_amd/build.py``); there is no fallback.
 
 Tensors are [B, H, S, D] bf16, contiguous, on one HIP device, with S = F * HH * WW tokens
 in frame-major order (t = f*HH*WW + y*WW + x) unless a function says token-major.
@@ -46,7 +46,7 @@ class SvgError(RuntimeError):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m spatial_temporal_sparse_amd.build`")
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python {os.path.join(_HERE, 'build.py')}`")
     lib = ctypes.CDLL(LIB_PATH)
     st = _c_i32
     sig = {

@@ -1,6 +1,8 @@
 """Build libsvg.so (the HIP kernels and the C ABI) for gfx950 with hipcc, in place.
 
-    python -m spatial_temporal_sparse_amd.build
+    python spatial_temporal_sparse_amd/build.py
+
+(run as a script: importing the package would first load the library being built)
 """
 from __future__ import annotations
 
