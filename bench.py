@@ -47,6 +47,10 @@ def parse():
                     help="layout transformation of temporal heads inside the attention kernel, or as separate "
                          "permute / unpermute passes")
     ap.add_argument("--no-compare", action="store_true", help="do not also time the other layout")
+    ap.add_argument("--denoise", type=int, default=0, metavar="N",
+                    help="instead: time the attention layers of an N-step denoising loop through the step driver "
+                         "(dense attention for the first quarter of the steps, then profiling + sparse attention), "
+                         "eager and with HIP-graph replay, and print that JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (the reference kernel that scales "
                          "the FETCH_SIZE / WRITE_SIZE counters to bytes) and exit")
@@ -137,10 +141,89 @@ def cpu_baseline(q, k, v, kinds, g, w_f, w_p):
             "seconds": round(elapsed, 2)}
 
 
+def denoise(args):
+    """Attention layers of an N-step denoising loop through svg.StepDriver (one svg_layer call,
+    or one graph replay, per layer).  Inputs are copied into the driver's buffers outside the
+    timed region, where a model's QKV projection would write them."""
+    import numpy as np
+    import torch
+
+    import spatial_temporal_sparse_amd as svg
+    from workloads import WORKLOADS, make_qkv, norm_weights, sample_queries
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = WORKLOADS["hunyuan720p_step"]
+    g = wl.geom
+    n_steps, L = args.denoise, max(1, args.layers)
+    log(f"[denoise] {n_steps} steps x {L} layers of {g}")
+    layers = []
+    for l in range(L):
+        q, k, v = make_qkv(wl, device="cuda", layer=l)
+        layers.append((q, k, v))
+    wq, wk = norm_weights(g.D, wl.seed)
+    norm = (torch.from_numpy(wq).to(dev), torch.from_numpy(wk).to(dev), wl.eps, wl.rope_base)
+    out = {}
+    for graphs in (False, True):
+        drv = svg.StepDriver(g.B, g.H, g.F, g.HH, g.WW, g.D, n_steps, wl.w_f, wl.w_p, n_q=wl.n_q, norm=norm,
+                             graphs=graphs, device=dev)
+
+        def loop(timed):
+            per_step = []
+            for s_ in range(n_steps):
+                evs = []
+                for l in range(L):
+                    q, k, v = layers[l]
+                    drv.q.copy_(q)
+                    drv.k.copy_(k)
+                    drv.v.copy_(v)
+                    drv.q_idx.copy_(torch.from_numpy(sample_queries(g.S, wl.n_q, wl.idx_seed + s_ * L + l)))
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    drv.layer(s_)
+                    e1.record()
+                    evs.append((e0, e1))
+                torch.cuda.synchronize()
+                per_step.append(sum(a.elapsed_time(b) for a, b in evs))
+            return per_step
+
+        loop(False)                 # warm-up (and, with graphs, capture)
+        per_step = loop(True)
+        dense = [drv.is_dense(s_) for s_ in range(n_steps)]
+        out[graphs] = (per_step, dense)
+        log(f"[denoise] graphs={graphs}: {[round(x, 2) for x in per_step]} ms per step")
+    per_step, dense = out[True]
+    eager = out[False][0]
+    d_ms = float(np.mean([t for t, d in zip(per_step, dense) if d])) if any(dense) else None
+    s_ms = float(np.mean([t for t, d in zip(per_step, dense) if not d])) if not all(dense) else None
+    mean = float(np.mean(per_step))
+    res = {
+        "metric": "denoising loop: attention ms per step (dense first quarter, then profiling + sparse), 720p shape",
+        "value": round(mean, 3), "unit": "ms", "higher_is_better": False, "n_gpus": 1, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"hunyuan720p_step: {n_steps} denoising steps x {L} attention layers "
+                               f"(QK-RMSNorm + 3D RoPE in every layer)", "dense_fraction": 0.25,
+                   "dense_steps": int(sum(dense)), "B": g.B, "H": g.H, "F": g.F, "HH": g.HH, "WW": g.WW, "D": g.D,
+                   "w_f": wl.w_f, "w_p": wl.w_p, "n_q": wl.n_q},
+        "dense_step_ms": None if d_ms is None else round(d_ms, 3),
+        "sparse_step_ms": None if s_ms is None else round(s_ms, 3),
+        "graph_ms_per_step": round(mean, 3),
+        "eager_ms_per_step": round(float(np.mean(eager)), 3),
+        "speedup_vs_all_dense": None if d_ms is None else round(d_ms / mean, 3),
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.denoise > 0:
+        if args.gpus != 1:
+            print("bench.py runs on one GPU only", file=sys.stderr)
+            sys.exit(2)
+        denoise(args)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards over heads with no "

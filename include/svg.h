@@ -57,6 +57,7 @@ typedef int32_t svg_status;
 /* Workspace-size queries. */
 #define SVG_OP_PROFILE     1
 #define SVG_OP_SPARSE_ATTN 2
+#define SVG_OP_LAYER       3
 
 typedef struct {
     int32_t B, H;       /* batch, heads */
@@ -170,6 +171,35 @@ svg_status svg_sparse_attn(const void* q, const void* k, const void* v,
  */
 svg_status svg_dense_attn(const void* q, const void* k, const void* v, svg_geom g, float scale, void* o,
                           void* stream);
+
+/*
+ * svg_layer -- one attention layer of a denoising step in one call: the per-layer pipeline
+ * of [svg-authors] (QK-Norm and RoPE, online profiling, sparse attention with the layout
+ * transformation) and its schedule of dense attention in the early steps ([svg-authors]
+ * other optimisations).  Enqueued in order on `stream`:
+ *   1. when wq or wk is given: svg_qknorm_rope of q, k into qn, kn (slice widths dt, dh, dw);
+ *      profiling and attention then read qn, kn.  Otherwise they read q, k, and qn, kn,
+ *      eps, rope_base and dt, dh, dw are ignored.
+ *   2. dense != 0: svg_dense_attn into o; q_idx, n_q, w, mse_out and kind_out are ignored.
+ *      dense == 0: svg_profile_heads (kinds into kind_out, errors into mse_out), then
+ *      svg_sparse_attn with the fused layout transformation into o.
+ * Arguments, layouts and limits are those of the calls named above; every stage is checked
+ * before any is enqueued.  o: bf16 [B][H][S][D] frame-major.
+ * ws: >= svg_workspace_bytes(SVG_OP_LAYER, &g, n_q) bytes (profiling and attention share it).
+ */
+svg_status svg_layer(const void* q, const void* k, const void* v, const float* wq, const float* wk, float eps,
+                     float rope_base, int32_t dt, int32_t dh, int32_t dw, void* qn, void* kn,
+                     const int32_t* q_idx, int32_t n_q, svg_geom g, svg_windows w, float scale, int32_t dense,
+                     void* o, float* mse_out, uint8_t* kind_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * svg_dense_step -- the step schedule of [svg-authors] other optimisations: the first
+ * dense_fraction of the n_steps denoising steps run dense attention, the rest sparse.
+ * Step s (0-based) runs dense iff s < dense_fraction * n_steps, i.e. the first
+ * ceil(dense_fraction * n_steps) steps.  Returns 1 (dense) or 0 (sparse);
+ * SVG_ERR_INVALID unless 0 <= step < n_steps and 0 <= dense_fraction <= 1.
+ */
+int32_t svg_dense_step(int32_t step, int32_t n_steps, float dense_fraction);
 
 /* Bytes of workspace a call needs (0 for an invalid request). */
 size_t svg_workspace_bytes(int32_t op, const svg_geom* g, int32_t n_q);

@@ -25,6 +25,7 @@ TEMPORAL = 1
 DENSE = 2
 OP_PROFILE = 1
 OP_SPARSE_ATTN = 2
+OP_LAYER = 3
 
 _c_i32 = ctypes.c_int32
 _c_vp = ctypes.c_void_p
@@ -60,6 +61,10 @@ def _load() -> ctypes.CDLL:
         "svg_sparse_attn": (st, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, Geom, Windows, ctypes.c_float,
                                  _c_vp, _c_vp, _c_vp, ctypes.c_size_t, _c_vp]),
         "svg_dense_attn": (st, [_c_vp, _c_vp, _c_vp, Geom, ctypes.c_float, _c_vp, _c_vp]),
+        "svg_layer": (st, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, ctypes.c_float, ctypes.c_float, _c_i32, _c_i32, _c_i32,
+                           _c_vp, _c_vp, _c_vp, _c_i32, Geom, Windows, ctypes.c_float, _c_i32, _c_vp, _c_vp, _c_vp,
+                           _c_vp, ctypes.c_size_t, _c_vp]),
+        "svg_dense_step": (_c_i32, [_c_i32, _c_i32, ctypes.c_float]),
         "svg_workspace_bytes": (ctypes.c_size_t, [_c_i32, ctypes.POINTER(Geom), _c_i32]),
         "svg_tile_shape": (None, [ctypes.POINTER(_c_i32), ctypes.POINTER(_c_i32)]),
         "svg_status_string": (ctypes.c_char_p, [_c_i32]),
@@ -302,3 +307,112 @@ def sparse_layer(q, k, v, q_idx, F, HH, WW, w_f, w_p, norm=None, scale=None, buf
                 ws=bufs.ws_attn)
     unpermute(bufs.ot, F, HH, WW, bufs.kind, TEMPORAL, out=bufs.o)
     return bufs.o, bufs.kind, bufs.mse, q, k
+
+
+def dense_step(step: int, n_steps: int, dense_fraction: float = 0.25) -> bool:
+    """True if denoising step `step` of `n_steps` runs dense attention (svg_dense_step): the
+    first dense_fraction of the steps do, i.e. steps with step < dense_fraction * n_steps."""
+    r = int(lib.svg_dense_step(int(step), int(n_steps), float(dense_fraction)))
+    if r < 0:
+        _check(r)
+    return r == 1
+
+
+def layer(q, k, v, q_idx, F, HH, WW, w_f, w_p, dense=False, norm=None, dims=None, scale=None, o=None, qn=None,
+          kn=None, mse=None, kind=None, ws=None):
+    """One attention layer in one library call (svg_layer): [QK-RMSNorm + 3D RoPE], then dense
+    attention (dense=True) or profiling + block-sparse attention with the fused layout
+    transformation.  norm: None or (wq, wk, eps, rope_base).  Returns (o, kind, mse, q', k'),
+    where q', k' are what attention read; kind and mse are not written by a dense layer."""
+    g = geometry(q, F, HH, WW)
+    shp = _shape(g)
+    dev = q.device
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check_qkv(n, t, shp, device=dev)
+    if q_idx.dtype != torch.int32 or q_idx.dim() != 1 or q_idx.device != dev or not q_idx.is_contiguous():
+        raise ValueError("q_idx must be a contiguous int32 [n_q] tensor on the same device")
+    n_q = q_idx.numel()
+    o = torch.empty_like(q) if o is None else o
+    _check_qkv("o", o, shp, device=dev)
+    mse = torch.empty((g.B, g.H, 2), dtype=torch.float32, device=dev) if mse is None else mse
+    kind = torch.empty((g.B, g.H), dtype=torch.uint8, device=dev) if kind is None else kind
+    _check_qkv("mse", mse, (g.B, g.H, 2), torch.float32, dev)
+    _check_qkv("kind", kind, (g.B, g.H), torch.uint8, dev)
+    wq = wk = None
+    eps, base = 1e-6, 10000.0
+    if norm is not None:
+        wq, wk, eps, base = norm
+        _check_qkv("wq", wq, (g.D,), torch.float32, dev)
+        _check_qkv("wk", wk, (g.D,), torch.float32, dev)
+        qn = torch.empty_like(q) if qn is None else qn
+        kn = torch.empty_like(k) if kn is None else kn
+        _check_qkv("qn", qn, shp, device=dev)
+        _check_qkv("kn", kn, shp, device=dev)
+    dt, dh, dw = rope_split(g.D) if dims is None else dims
+    ws = _workspace(OP_LAYER, g, n_q, dev, ws)
+    sc = default_scale(g.D) if scale is None else scale
+    _check(lib.svg_layer(_ptr(q), _ptr(k), _ptr(v), _ptr(wq), _ptr(wk), float(eps), float(base), dt, dh, dw,
+                         _ptr(qn), _ptr(kn), _ptr(q_idx), n_q, g, Windows(w_f, w_p), float(sc), int(bool(dense)),
+                         _ptr(o), _ptr(mse), _ptr(kind), _ptr(ws), ws.numel(), _stream(q)))
+    return o, kind, mse, (qn if norm is not None else q), (kn if norm is not None else k)
+
+
+class StepDriver:
+    """The attention layers of a denoising loop on one device.
+
+    Each layer is one svg_layer call on the driver's static buffers: the caller writes the
+    layer's inputs into `q`, `k`, `v` (bf16 [B, H, S, D], frame-major) and `q_idx` (int32
+    [n_q] sampled rows), then calls `layer(step)`, which leaves the output in `o` (and, for a
+    sparse step, the head kinds and errors in `kind`, `mse`).  Steps with
+    dense_step(step, n_steps, dense_fraction) run dense attention, the others profile and run
+    sparse attention.  With graphs=True the dense and the sparse layer are each captured once
+    in a HIP graph (torch.cuda.CUDAGraph) on first use and replayed afterwards; nothing is
+    allocated per layer either way.
+    """
+
+    def __init__(self, B, H, F, HH, WW, D, n_steps, w_f, w_p, n_q=64, norm=None, dense_fraction=0.25, scale=None,
+                 graphs=False, device="cuda"):
+        self.F, self.HH, self.WW = F, HH, WW
+        self.n_steps, self.dense_fraction = int(n_steps), float(dense_fraction)
+        self.w_f, self.w_p, self.scale = w_f, w_p, scale
+        self.graphs = bool(graphs)
+        dev = torch.device(device)
+        shp = (B, H, F * HH * WW, D)
+        self.q, self.k, self.v, self.o = (torch.zeros(shp, dtype=torch.bfloat16, device=dev) for _ in range(4))
+        self.q_idx = torch.zeros((n_q,), dtype=torch.int32, device=dev)
+        self.mse = torch.zeros((B, H, 2), dtype=torch.float32, device=dev)
+        self.kind = torch.zeros((B, H), dtype=torch.uint8, device=dev)
+        self.norm = None
+        self.qn = self.kn = None
+        if norm is not None:
+            wq, wk, eps, base = norm
+            self.norm = (wq.to(dev).contiguous(), wk.to(dev).contiguous(), float(eps), float(base))
+            self.qn, self.kn = torch.empty_like(self.q), torch.empty_like(self.k)
+        g = geometry(self.q, F, HH, WW)
+        self.ws = torch.empty(max(256, workspace_bytes(OP_LAYER, g, n_q)), dtype=torch.uint8, device=dev)
+        self._graph = {}
+
+    def is_dense(self, step: int) -> bool:
+        return dense_step(step, self.n_steps, self.dense_fraction)
+
+    def _run(self, dense: bool) -> None:
+        layer(self.q, self.k, self.v, self.q_idx, self.F, self.HH, self.WW, self.w_f, self.w_p, dense=dense,
+              norm=self.norm, scale=self.scale, o=self.o, qn=self.qn, kn=self.kn, mse=self.mse, kind=self.kind,
+              ws=self.ws)
+
+    def layer(self, step: int):
+        """Runs one layer of denoising step `step` on the static inputs; returns (o, kind, mse)."""
+        dense = self.is_dense(step)
+        if not self.graphs:
+            self._run(dense)
+            return self.o, self.kind, self.mse
+        g = self._graph.get(dense)
+        if g is None:
+            self._run(dense)                      # eager first run (the graph is captured after it)
+            torch.cuda.current_stream(self.q.device).synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self._run(dense)
+            self._graph[dense] = g
+        g.replay()
+        return self.o, self.kind, self.mse

@@ -80,9 +80,9 @@ size_t attn_ws_bytes(const svg_geom& g) { return align_up((size_t)g.B * g.H * si
 
 }  // namespace
 
-SVG_API svg_status svg_qknorm_rope(const void* q, const void* k, void* q_out, void* k_out, const float* wq,
-                                   const float* wk, float eps, float rope_base, int32_t dt, int32_t dh, int32_t dw,
-                                   svg_geom g, void* stream) {
+static svg_status svg_qknorm_rope_impl(const void* q, const void* k, void* q_out, void* k_out, const float* wq,
+                                       const float* wk, float eps, float rope_base, int32_t dt, int32_t dh, int32_t dw,
+                                       svg_geom g, void* stream, bool launch) {
   svg_status s;
   if ((s = check_geom(g, true)) != SVG_OK) return s;
   if ((s = check_ptrs({{q, "q"}, {k, "k"}, {q_out, "q_out"}, {k_out, "k_out"}, {wq, "wq"}, {wk, "wk"}})) != SVG_OK)
@@ -94,6 +94,7 @@ SVG_API svg_status svg_qknorm_rope(const void* q, const void* k, void* q_out, vo
   const int64_t entries = (int64_t)g.F * (dt / 2) + (int64_t)g.HH * (dh / 2) + (int64_t)g.WW * (dw / 2);
   if (entries * 8 > 64 * 1024)
     return fail(SVG_ERR_UNSUPPORTED, "rope tables (%lld entries) exceed 64 KiB of LDS", (long long)entries);
+  if (!launch) return SVG_OK;
   svg::RopeArgs a;
   a.in[0] = (const svg::bf16*)q;
   a.in[1] = (const svg::bf16*)k;
@@ -119,6 +120,12 @@ SVG_API svg_status svg_qknorm_rope(const void* q, const void* k, void* q_out, vo
   return hip_status(svg::launch_qknorm_rope(a, (hipStream_t)stream), "svg_qknorm_rope");
 }
 
+SVG_API svg_status svg_qknorm_rope(const void* q, const void* k, void* q_out, void* k_out, const float* wq,
+                                   const float* wk, float eps, float rope_base, int32_t dt, int32_t dh, int32_t dw,
+                                   svg_geom g, void* stream) {
+  return svg_qknorm_rope_impl(q, k, q_out, k_out, wq, wk, eps, rope_base, dt, dh, dw, g, stream, true);
+}
+
 // The attention and profiling kernels address a head's rows with 32-bit byte offsets.
 static svg_status check_head_bytes(const svg_geom& g) {
   const int64_t S = (int64_t)g.F * g.HH * g.WW;
@@ -127,9 +134,9 @@ static svg_status check_head_bytes(const svg_geom& g) {
   return SVG_OK;
 }
 
-SVG_API svg_status svg_profile_heads(const void* q, const void* k, const void* v, const int32_t* q_idx, int32_t n_q,
-                                     svg_geom g, svg_windows w, float scale, float* mse_out, uint8_t* kind_out,
-                                     void* ws, size_t ws_bytes, void* stream) {
+static svg_status svg_profile_heads_impl(const void* q, const void* k, const void* v, const int32_t* q_idx, int32_t n_q,
+                                         svg_geom g, svg_windows w, float scale, float* mse_out, uint8_t* kind_out,
+                                         void* ws, size_t ws_bytes, void* stream, bool launch) {
   svg_status s;
   if ((s = check_geom(g, true)) != SVG_OK) return s;
   if ((s = check_windows(w)) != SVG_OK) return s;
@@ -146,6 +153,7 @@ SVG_API svg_status svg_profile_heads(const void* q, const void* k, const void* v
   if (ws == nullptr || ws_bytes < need)
     return fail(SVG_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws == nullptr ? (size_t)0 : ws_bytes);
   if (!aligned16(ws)) return fail(SVG_ERR_INVALID, "ws is not 16-byte aligned");
+  if (!launch) return SVG_OK;
   svg::ProfilePlan plan = svg::profile_plan(g.B * g.H, S, g.D, n_q);
   svg::ProfileArgs a;
   a.q = (const svg::bf16*)q;
@@ -171,6 +179,12 @@ SVG_API svg_status svg_profile_heads(const void* q, const void* k, const void* v
   a.mse = mse_out;
   a.kind = kind_out;
   return hip_status(svg::launch_profile(a, (hipStream_t)stream), "svg_profile_heads");
+}
+
+SVG_API svg_status svg_profile_heads(const void* q, const void* k, const void* v, const int32_t* q_idx, int32_t n_q,
+                                     svg_geom g, svg_windows w, float scale, float* mse_out, uint8_t* kind_out,
+                                     void* ws, size_t ws_bytes, void* stream) {
+  return svg_profile_heads_impl(q, k, v, q_idx, n_q, g, w, scale, mse_out, kind_out, ws, ws_bytes, stream, true);
 }
 
 static svg_status permute_common(const void* src, void* dst, int32_t elem_bytes, const uint8_t* kind, int32_t select,
@@ -251,9 +265,9 @@ static void fill_attn(svg::AttnArgs& a, svg_geom g, svg_windows w, float scale) 
   a.scale = scale;
 }
 
-SVG_API svg_status svg_sparse_attn(const void* q, const void* k, const void* v, const void* qt, const void* kt,
-                                   const void* vt, const uint8_t* kind, svg_geom g, svg_windows w, float scale, void* o,
-                                   void* ot, void* ws, size_t ws_bytes, void* stream) {
+static svg_status svg_sparse_attn_impl(const void* q, const void* k, const void* v, const void* qt, const void* kt,
+                                       const void* vt, const uint8_t* kind, svg_geom g, svg_windows w, float scale, void* o,
+                                       void* ot, void* ws, size_t ws_bytes, void* stream, bool launch) {
   svg_status s;
   if ((s = check_geom(g, true)) != SVG_OK) return s;
   if ((s = check_windows(w)) != SVG_OK) return s;
@@ -269,6 +283,7 @@ SVG_API svg_status svg_sparse_attn(const void* q, const void* k, const void* v, 
   if (kind != nullptr && (ws == nullptr || ws_bytes < need))
     return fail(SVG_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws == nullptr ? (size_t)0 : ws_bytes);
   if (kind != nullptr && ((uintptr_t)ws & 3u)) return fail(SVG_ERR_INVALID, "ws is not 4-byte aligned");
+  if (!launch) return SVG_OK;
   svg::AttnArgs a;
   a.q = (const svg::bf16*)q;
   a.k = (const svg::bf16*)k;
@@ -286,13 +301,20 @@ SVG_API svg_status svg_sparse_attn(const void* q, const void* k, const void* v, 
   return hip_status(svg::launch_attention(a, (hipStream_t)stream), "svg_sparse_attn");
 }
 
-SVG_API svg_status svg_dense_attn(const void* q, const void* k, const void* v, svg_geom g, float scale, void* o,
-                                  void* stream) {
+SVG_API svg_status svg_sparse_attn(const void* q, const void* k, const void* v, const void* qt, const void* kt,
+                                   const void* vt, const uint8_t* kind, svg_geom g, svg_windows w, float scale, void* o,
+                                   void* ot, void* ws, size_t ws_bytes, void* stream) {
+  return svg_sparse_attn_impl(q, k, v, qt, kt, vt, kind, g, w, scale, o, ot, ws, ws_bytes, stream, true);
+}
+
+static svg_status svg_dense_attn_impl(const void* q, const void* k, const void* v, svg_geom g, float scale, void* o,
+                                      void* stream, bool launch) {
   svg_status s;
   if ((s = check_geom(g, true)) != SVG_OK) return s;
   if ((s = check_ptrs({{q, "q"}, {k, "k"}, {v, "v"}, {o, "o"}})) != SVG_OK) return s;
   if ((s = check_head_bytes(g)) != SVG_OK) return s;
   if (!(scale > 0.f) || !std::isfinite(scale)) return fail(SVG_ERR_INVALID, "scale must be finite and > 0");
+  if (!launch) return SVG_OK;
   svg::AttnArgs a;
   a.fused_t = 0;
   a.q = a.qt = (const svg::bf16*)q;
@@ -304,6 +326,52 @@ SVG_API svg_status svg_dense_attn(const void* q, const void* k, const void* v, s
   a.force_dense = 1;
   fill_attn(a, g, svg_windows{0, 0}, scale);
   return hip_status(svg::launch_attention(a, (hipStream_t)stream), "svg_dense_attn");
+}
+
+SVG_API svg_status svg_dense_attn(const void* q, const void* k, const void* v, svg_geom g, float scale, void* o,
+                                  void* stream) {
+  return svg_dense_attn_impl(q, k, v, g, scale, o, stream, true);
+}
+
+// svg_layer runs profiling and attention one after the other on its stream, so they share
+// one workspace.
+static size_t layer_ws_bytes(const svg_geom& g, int32_t n_q) {
+  const size_t p = profile_ws_bytes(g, n_q), a = attn_ws_bytes(g);
+  return p > a ? p : a;
+}
+
+SVG_API int32_t svg_dense_step(int32_t step, int32_t n_steps, float dense_fraction) {
+  if (n_steps <= 0 || step < 0 || step >= n_steps || !(dense_fraction >= 0.f && dense_fraction <= 1.f))
+    return fail(SVG_ERR_INVALID, "step=%d of n_steps=%d, dense_fraction=%g: need 0 <= step < n_steps, fraction in [0, 1]",
+                step, n_steps, (double)dense_fraction);
+  return (double)step < (double)dense_fraction * (double)n_steps ? 1 : 0;
+}
+
+SVG_API svg_status svg_layer(const void* q, const void* k, const void* v, const float* wq, const float* wk, float eps,
+                             float rope_base, int32_t dt, int32_t dh, int32_t dw, void* qn, void* kn,
+                             const int32_t* q_idx, int32_t n_q, svg_geom g, svg_windows w, float scale, int32_t dense,
+                             void* o, float* mse_out, uint8_t* kind_out, void* ws, size_t ws_bytes, void* stream) {
+  const bool norm = wq != nullptr || wk != nullptr;
+  const void* qa = norm ? qn : q;       // what profiling and attention read
+  const void* ka = norm ? kn : k;
+  // pass 0 checks every stage, pass 1 enqueues them: a failed check enqueues nothing
+  for (int pass = 0; pass < 2; ++pass) {
+    const bool launch = pass == 1;
+    svg_status s;
+    if (norm && (s = svg_qknorm_rope_impl(q, k, qn, kn, wq, wk, eps, rope_base, dt, dh, dw, g, stream, launch)) != SVG_OK)
+      return s;
+    if (dense) {
+      if ((s = svg_dense_attn_impl(qa, ka, v, g, scale, o, stream, launch)) != SVG_OK) return s;
+    } else {
+      if ((s = svg_profile_heads_impl(qa, ka, v, q_idx, n_q, g, w, scale, mse_out, kind_out, ws, ws_bytes, stream,
+                                      launch)) != SVG_OK)
+        return s;
+      if ((s = svg_sparse_attn_impl(qa, ka, v, nullptr, nullptr, nullptr, kind_out, g, w, scale, o, nullptr, ws,
+                                    ws_bytes, stream, launch)) != SVG_OK)
+        return s;
+    }
+  }
+  return SVG_OK;
 }
 
 SVG_API size_t svg_workspace_bytes(int32_t op, const svg_geom* g, int32_t n_q) {
@@ -319,6 +387,11 @@ SVG_API size_t svg_workspace_bytes(int32_t op, const svg_geom* g, int32_t n_q) {
     return profile_ws_bytes(*g, n_q);
   }
   if (op == SVG_OP_SPARSE_ATTN) return attn_ws_bytes(*g);
+  if (op == SVG_OP_LAYER) {
+    const int32_t S = g->F * g->HH * g->WW;
+    if (n_q < 1 || n_q > S) return 0;
+    return layer_ws_bytes(*g, n_q);
+  }
   return 0;
 }
 

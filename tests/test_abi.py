@@ -29,8 +29,8 @@ def svg():
 def test_header_declares_the_path():
     names = _declared_functions()
     for n in ("svg_qknorm_rope", "svg_profile_heads", "svg_permute", "svg_unpermute", "svg_build_block_mask",
-              "svg_sparse_attn", "svg_dense_attn", "svg_workspace_bytes", "svg_tile_shape", "svg_status_string",
-              "svg_last_error"):
+              "svg_sparse_attn", "svg_dense_attn", "svg_layer", "svg_dense_step", "svg_workspace_bytes",
+              "svg_tile_shape", "svg_status_string", "svg_last_error"):
         assert n in names
 
 
@@ -63,6 +63,19 @@ def test_workspace_sizes(svg):
     assert svg.workspace_bytes(svg.OP_PROFILE, g, 0) == 0                  # n_q out of range
     assert svg.workspace_bytes(svg.OP_PROFILE, svg.Geom(1, 24, 33, 45, 80, 96), 64) == 0   # D unsupported
     assert svg.workspace_bytes(99, g, 64) == 0
+    # a layer runs profiling and attention one after the other on one workspace
+    assert svg.workspace_bytes(svg.OP_LAYER, g, 64) == max(ws, 256)
+    assert svg.workspace_bytes(svg.OP_LAYER, g, 0) == 0
+
+
+def test_dense_step_schedule(svg):
+    # the first quarter of the steps (step < 0.25 * n_steps) run dense
+    assert [svg.dense_step(s, 4) for s in range(4)] == [True, False, False, False]
+    assert [s for s in range(50) if svg.dense_step(s, 50)] == list(range(13))
+    assert not any(svg.dense_step(s, 8, 0.0) for s in range(8))
+    assert all(svg.dense_step(s, 8, 1.0) for s in range(8))
+    for bad in ((4, 4, 0.25), (-1, 4, 0.25), (0, 0, 0.25), (0, 4, 1.5), (0, 4, -0.1)):
+        assert svg.lib.svg_dense_step(*bad) == -1
 
 
 FAKE = ctypes.c_void_p(0x100000)   # never dereferenced: each call below fails a host check first
@@ -111,6 +124,23 @@ def test_argument_checks(svg):
                              1 << 20, None) == -2
     assert L.svg_profile_heads(FAKE, FAKE, FAKE, FAKE, 64, big, W(1, 2), 0.125, FAKE, FAKE, FAKE, 1 << 20,
                                None) == -2
+    # svg_layer checks every stage before it enqueues any: here the norm stage is valid and the
+    # profiling stage is not, and the call returns that stage's status
+    F2, F3, F4 = (ctypes.c_void_p(a) for a in (0x200000, 0x300000, 0x400000))
+    assert L.svg_layer(FAKE, FAKE, FAKE, FAKE, FAKE, 1e-6, 1e4, 24, 20, 20, F2, F3, FAKE, 0, good, W(1, 2), 0.125, 0,
+                       F4, FAKE, FAKE, FAKE, 1 << 30, None) == -1
+    assert L.svg_layer(FAKE, FAKE, FAKE, FAKE, FAKE, 1e-6, 1e4, 24, 20, 20, F2, F3, FAKE, 64, good, W(1, 2), 0.125, 0,
+                       F4, FAKE, FAKE, FAKE, 16, None) == -4
+    # normalised outputs are required when the norm runs, and the rope slices must fit D
+    assert L.svg_layer(FAKE, FAKE, FAKE, FAKE, FAKE, 1e-6, 1e4, 24, 20, 20, None, F3, FAKE, 64, good, W(1, 2), 0.125, 1,
+                       F4, None, None, None, 0, None) == -1
+    assert L.svg_layer(FAKE, FAKE, FAKE, FAKE, FAKE, 1e-6, 1e4, 24, 22, 20, F2, F3, FAKE, 64, good, W(1, 2), 0.125, 1,
+                       F4, None, None, None, 0, None) == -1
+    # a dense layer still needs its output and a positive scale
+    assert L.svg_layer(FAKE, FAKE, FAKE, None, None, 0.0, 0.0, 0, 0, 0, None, None, None, 0, good, W(0, 0), 0.125, 1,
+                       None, None, None, None, 0, None) == -1
+    assert L.svg_layer(FAKE, FAKE, FAKE, None, None, 0.0, 0.0, 0, 0, 0, None, None, None, 0, good, W(0, 0), 0.0, 1,
+                       F4, None, None, None, 0, None) == -1
     # rope slices must be even and add up to D; eps must be positive
     assert L.svg_qknorm_rope(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1e-6, 1e4, 24, 21, 19, good, None) == -1
     assert L.svg_qknorm_rope(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.0, 1e4, 24, 20, 20, good, None) == -1
