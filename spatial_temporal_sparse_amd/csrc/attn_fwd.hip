@@ -110,7 +110,8 @@ __global__ void head_order_kernel(const uint8_t* __restrict__ kind, int32_t* __r
 // publishes them, one phase (K) or two phases (V) before their first reader.  So no copy is
 // in flight during an M phase; each M phase still starts with an explicit wait on vector
 // memory (free at run time) so that the compiler knows it and counts the LDS waits instead
-// of draining them.  The K buffers are two distinct LDS objects and the phase loop is
+// of draining them.  After that wait at the end of its X phase, a group reads the first V^T
+// operand of its next M phase: that V tile was published a phase earlier.  The K buffers are two distinct LDS objects and the phase loop is
 // unrolled by four, so every K access names one of them.
 // ------------------------------------------------------------------------------------------
 constexpr int PP_BM = 256;        // query rows per workgroup
@@ -158,8 +159,26 @@ __device__ __forceinline__ void phase_qk(RowState<D>& st, const bf16x8 (&qf)[D /
 }
 
 // O^T += V^T P^T for the 64 keys of a tile (four 16-key steps).
+// V^T operands of a matrix phase's first PV products that its wavefront reads at the end of its
+// previous (vector) phase, so that the phase opens with an MFMA instead of an LDS wait (deeper
+// prefetch measured no better)
+constexpr int NPRE = 1;
+// V^T operand of PV step 0, d block j
 template <int D>
-__device__ __forceinline__ void phase_pv(RowState<D>& st, const char* vbase, int v_row, int v_col) {
+__device__ __forceinline__ bf16x8 read_vt0(const char* vbase, int v_row, int v_col, int j) {
+  using T = TileLds<D>;
+  const char* v0 = vbase + v_row * T::ROW_BYTES;
+  const char* v1 = v0 + 8 * T::ROW_BYTES;
+  const int col = 32 * j + v_col;
+  const int cb = 2 * (col & 7);
+  const i16x4 lo = lds_read_tr(reinterpret_cast<const bf16*>(v0 + 16 * ((col >> 3) ^ T::swz_v(v_row)) + cb));
+  const i16x4 hi = lds_read_tr(reinterpret_cast<const bf16*>(v1 + 16 * ((col >> 3) ^ T::swz_v(v_row + 8)) + cb));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+template <int D>
+__device__ __forceinline__ void phase_pv(RowState<D>& st, const char* vbase, int v_row, int v_col,
+                                         const bf16x8 (&av0)[NPRE]) {
   using T = TileLds<D>;
   constexpr int NDB = D / 32;
 #pragma unroll
@@ -170,11 +189,16 @@ __device__ __forceinline__ void phase_pv(RowState<D>& st, const char* vbase, int
     const int sw0 = T::swz_v(r0), sw1 = T::swz_v(r0 + 8);
 #pragma unroll
     for (int j = 0; j < NDB; ++j) {
-      const int col = 32 * j + v_col;       // logical element column
-      const int cb = 2 * (col & 7);         // byte inside the 16-byte chunk
-      const i16x4 lo = lds_read_tr(reinterpret_cast<const bf16*>(v0 + 16 * ((col >> 3) ^ sw0) + cb));
-      const i16x4 hi = lds_read_tr(reinterpret_cast<const bf16*>(v1 + 16 * ((col >> 3) ^ sw1) + cb));
-      const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      bf16x8 av;
+      if (s == 0 && j < NPRE) {
+        av = av0[j];                        // read at the end of the previous phase
+      } else {
+        const int col = 32 * j + v_col;     // logical element column
+        const int cb = 2 * (col & 7);       // byte inside the 16-byte chunk
+        const i16x4 lo = lds_read_tr(reinterpret_cast<const bf16*>(v0 + 16 * ((col >> 3) ^ sw0) + cb));
+        const i16x4 hi = lds_read_tr(reinterpret_cast<const bf16*>(v1 + 16 * ((col >> 3) ^ sw1) + cb));
+        av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
       st.oacc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, st.pb[s], st.oacc[j], 0, 0, 0);
     }
   }
@@ -184,22 +208,31 @@ __device__ __forceinline__ void phase_pv(RowState<D>& st, const char* vbase, int
 // QK (NQK MFMAs, one 16-byte read each) as one region: before MFMA m the reads of MFMAs up to
 // m + AHM have been issued, across the PV -> QK boundary.
 template <int NPV>
-constexpr int m_reads_upto(int m) { return m < NPV ? 2 * (m + 1) : 2 * NPV + (m + 1 - NPV); }
+constexpr int m_reads_upto(int m) {
+  const int r = (m < NPV ? 2 * (m + 1) : 2 * NPV + (m + 1 - NPV)) - 2 * NPRE;
+  return r > 0 ? r : 0;
+}
 template <int M_, int NPV, int NQK, int AHM, int ISSUED>
 __device__ __forceinline__ void order_m_phase() {
   if constexpr (M_ < NPV + NQK) {
     constexpr int last = M_ + AHM < NPV + NQK - 1 ? M_ + AHM : NPV + NQK - 1;
     constexpr int want = m_reads_upto<NPV>(last);
-    if constexpr (want > ISSUED) __builtin_amdgcn_sched_group_barrier(0x100, want - ISSUED, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (M_ < NPRE) {
+      // the first MFMAs' operands are already in registers: they go first
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if constexpr (want > ISSUED) __builtin_amdgcn_sched_group_barrier(0x100, want - ISSUED, 0);
+    } else {
+      if constexpr (want > ISSUED) __builtin_amdgcn_sched_group_barrier(0x100, want - ISSUED, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
     order_m_phase<M_ + 1, NPV, NQK, AHM, (want > ISSUED ? want : ISSUED)>();
   }
 }
 // One M phase: PV of the previous tile, then QK of the current one, as one region.
 template <int D>
 __device__ __forceinline__ void phase_m(RowState<D>& st, const bf16x8 (&qf)[D / 16], const char* vbase, const char* kb,
-                                        int v_row, int v_col, int l32, int hh) {
-  phase_pv<D>(st, vbase, v_row, v_col);
+                                        int v_row, int v_col, int l32, int hh, const bf16x8 (&av0)[NPRE]) {
+  phase_pv<D>(st, vbase, v_row, v_col, av0);
   phase_qk<D>(st, qf, kb, l32, hh);
   order_m_phase<0, (BN / 16) * (D / 32), 2 * (D / 16), SVG_ATTN_M_AHEAD, 0>();
 }
@@ -406,10 +439,18 @@ __global__ __launch_bounds__(PP_NT, 1) void attn_fwd_kernel(AttnArgs a, int32_t 
   };
   // M(i): PV(i-1) reads vprev, QK(i) reads kcur.  M(0) adds P^T = 0 times the zeroed V buffer;
   // the scores of the tile past the end (stale K buffer) are masked away by X(T).
+  bf16x8 av0[NPRE];
+#pragma unroll
+  for (int j = 0; j < NPRE; ++j) av0[j] = read_vt0<D>(reinterpret_cast<const char*>(Vb[2]), v_row, v_col, j);
   auto do_m = [&](const bf16* vprev, const bf16* kcur) {
     __builtin_amdgcn_s_waitcnt(VMCNT0);
     phase_m<D>(st, qf, reinterpret_cast<const char*>(vprev), reinterpret_cast<const char*>(kcur), v_row, v_col, l32,
-               hh);
+               hh, av0);
+  };
+  // after a group's vector phase and its copies: the first V^T operand of its next matrix phase
+  auto pre = [&](const bf16* vnext) {
+#pragma unroll
+    for (int j = 0; j < NPRE; ++j) av0[j] = read_vt0<D>(reinterpret_cast<const char*>(vnext), v_row, v_col, j);
   };
   auto do_x = [&](int32_t i) {
     __builtin_amdgcn_s_setprio(0);
@@ -434,6 +475,7 @@ __global__ __launch_bounds__(PP_NT, 1) void attn_fwd_kernel(AttnArgs a, int32_t 
     } else {
       do_x(2 * m - 1);
       __builtin_amdgcn_s_waitcnt(VMCNT0);
+      pre(vbuf(2 * m - 1));
     }
     phase_barrier();
     if (4 * m + 1 >= n_phase) break;
@@ -441,6 +483,7 @@ __global__ __launch_bounds__(PP_NT, 1) void attn_fwd_kernel(AttnArgs a, int32_t 
     if (grp == 0) {
       do_x(2 * m);
       __builtin_amdgcn_s_waitcnt(VMCNT0);
+      pre(vbuf(2 * m));
     } else {
       do_m(vbuf(2 * m - 1), K0);
       copy_v(2 * m);
@@ -454,6 +497,7 @@ __global__ __launch_bounds__(PP_NT, 1) void attn_fwd_kernel(AttnArgs a, int32_t 
     } else {
       do_x(2 * m);
       __builtin_amdgcn_s_waitcnt(VMCNT0);
+      pre(vbuf(2 * m));
     }
     phase_barrier();
     if (4 * m + 3 >= n_phase) break;
@@ -461,6 +505,7 @@ __global__ __launch_bounds__(PP_NT, 1) void attn_fwd_kernel(AttnArgs a, int32_t 
     if (grp == 0) {
       do_x(2 * m + 1);
       __builtin_amdgcn_s_waitcnt(VMCNT0);
+      pre(vbuf(2 * m + 1));
     } else {
       do_m(vbuf(2 * m), K1);
       copy_v(2 * m + 1);
