@@ -47,6 +47,9 @@ def parse():
                     help="layout transformation of temporal heads inside the attention kernel, or as separate "
                          "permute / unpermute passes")
     ap.add_argument("--no-compare", action="store_true", help="do not also time the other layout")
+    ap.add_argument("--workload", choices=("hunyuan720p_step", "cogvideox", "wan"), default="hunyuan720p_step",
+                    help="token grid of the step (default: the HunyuanVideo-720p layer the headline is quoted on; "
+                         "the others are the CogVideoX-like D=64 and the Wan-like grids)")
     ap.add_argument("--denoise", type=int, default=0, metavar="N",
                     help="instead: time the attention layers of an N-step denoising loop through the step driver "
                          "(dense attention for the first quarter of the steps, then profiling + sparse attention), "
@@ -112,7 +115,7 @@ def measured_traffic():
 
 def cpu_baseline(q, k, v, kinds, g, w_f, w_p):
     """The fp64 oracle on a bounded sample of the same layer: 6144 query rows of one spatial
-    and one temporal head against all 118800 keys; token-level FLOPs / wall time."""
+    and one temporal head against all S keys; token-level FLOPs / wall time."""
     import numpy as np
     import oracle.svg_oracle as O
     try:
@@ -137,7 +140,7 @@ def cpu_baseline(q, k, v, kinds, g, w_f, w_p):
         flops += 4.0 * g.D * float(m.sum())
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": "fp64 numpy oracle, sparse attention of 6144 sampled query rows of one spatial and one "
-                      "temporal head of the 720p layer (S=118800, D=128) against all keys; token-level FLOPs",
+                      f"temporal head of the layer (S={g.S}, D={g.D}) against all keys; token-level FLOPs",
             "seconds": round(elapsed, 2)}
 
 
@@ -237,7 +240,8 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    wl = WORKLOADS["hunyuan720p_step"]
+    wl = WORKLOADS[args.workload]
+    headline = args.workload == "hunyuan720p_step"
     g = wl.geom
     L = max(1, args.layers)
     log(f"[bench] generating {L} layers of {g} on {torch.cuda.get_device_name(dev)}")
@@ -350,10 +354,11 @@ def main():
     dense_ms = e0.elapsed_time(e1)
     dense_flops = 4.0 * S * S * D * BH
 
-    traffic = measured_traffic()
+    traffic = measured_traffic() if headline else None    # the counters were taken on the 720p layer
     tile_per_launch = float(step_tile.mean())
     result = {
-        "metric": "sparse-attn ms/layer + effective TFLOP/s (% bf16 MFMA peak), 720p shape",
+        "metric": "sparse-attn ms/layer + effective TFLOP/s (% bf16 MFMA peak), "
+                  + ("720p shape" if headline else f"{wl.name} shape"),
         "value": round(float(np.mean(step_tile)) / (ms_per_step * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -365,8 +370,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "hunyuan720p_step: one layer (qknorm+rope, profile 64 queries, layout "
-                               "transformation of temporal heads, block-sparse attention) over 4 layers of "
+        "config": {"workload": f"{wl.name}: one layer (qknorm+rope, profile {wl.n_q} queries, layout "
+                               f"transformation of temporal heads, block-sparse attention) over {L} layers of "
                                "fresh inputs",
                    "layout": args.layout,
                    "B": g.B, "H": g.H, "F": g.F, "HH": g.HH, "WW": g.WW, "S": S, "D": D, "w_f": w_f, "w_p": w_p,
@@ -385,7 +390,7 @@ def main():
         "compare": compare,
         "hbm_gbs": {k: round(v, 1) for k, v in hbm.items()},
         "hbm_frac_of_peak": {k: round(v / PEAK_HBM_GBS, 3) for k, v in hbm.items()},
-        "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel<128>", "achieved": round(attn_tflops, 2),
+        "roofline": {"bound": "mfma", "kernel": f"attn_fwd_kernel<{D}>", "achieved": round(attn_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
     }
