@@ -31,7 +31,8 @@
 //   per-lane scalar.  It is applied lazily: the running max only moves when a tile's max
 //   exceeds it by more than 8 (log2 units), which bounds p by 2^8 and skips most rescales.
 // exp2 with log2(e) folded into the softmax scale; fp32 accumulation; P rounded to bf16 for
-// the PV product; output divided by the row sum and rounded to bf16 (round-to-nearest-even).
+// the PV product; output divided by the row sum of those bf16 weights (so they sum to 1) and
+// rounded to bf16 (round-to-nearest-even).
 #include "svg_internal.h"
 
 namespace svg {
@@ -269,20 +270,28 @@ __device__ __forceinline__ void phase_softmax(RowState<D>& st, int32_t k0, bool 
     st.m_ref = m_new;
   }
   const float m_use = (st.m_ref == -INFINITY) ? 0.f : st.m_ref;
-  float rsum = 0.f;
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(st.sacc[blk][r], c, -m_use));
-      st.sacc[blk][r] = p;
-      rsum += p;
-    }
-  st.l_run += rsum;
+    for (int r = 0; r < 16; ++r) st.sacc[blk][r] = __builtin_amdgcn_exp2f(fmaf(st.sacc[blk][r], c, -m_use));
 #pragma unroll
   for (int s = 0; s < BN / 16; ++s)
 #pragma unroll
     for (int e = 0; e < 8; ++e) st.pb[s][e] = (bf16)st.sacc[s >> 1][8 * (s & 1) + e];
+  // row sum of the bf16 weights the PV product uses, two at a time (v_dot2_f32_bf16 against
+  // (1, 1)), in two independent chains
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+  float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+  for (int s = 0; s < BN / 16; ++s) {
+    const bf16x8 q = st.pb[s];
+    rs0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(q, q, 0, 1), one, rs0, false);
+    rs1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(q, q, 2, 3), one, rs1, false);
+    rs0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(q, q, 4, 5), one, rs0, false);
+    rs1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(q, q, 6, 7), one, rs1, false);
+  }
+  st.l_run += rs0 + rs1;
 }
 
 // Workgroup barrier without a memory fence.  The only data one wavefront hands another
