@@ -93,10 +93,16 @@ def token_flops(kind_np, g, w_f, w_p):
 
 
 def kernel_sha():
+    """Hash of the attention kernel's code (comments and whitespace ignored), which the stored
+    traffic counters were taken on."""
+    import re
     h = hashlib.sha256()
     for f in ("attn_fwd.hip", "svg_internal.h"):
-        with open(os.path.join(ROOT, "spatial_temporal_sparse_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "spatial_temporal_sparse_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -112,8 +112,9 @@ __global__ void head_order_kernel(const uint8_t* __restrict__ kind, int32_t* __r
 // in flight during an M phase; each M phase still starts with an explicit wait on vector
 // memory (free at run time) so that the compiler knows it and counts the LDS waits instead
 // of draining them.  After that wait at the end of its X phase, a group reads the first V^T
-// operand of its next M phase: that V tile was published a phase earlier.  The K buffers are two distinct LDS objects and the phase loop is
-// unrolled by four, so every K access names one of them.
+// operand of its next M phase: that V tile was published a phase earlier.  The K buffers are
+// two distinct LDS objects and the phase loop is unrolled by four, so every K access names one
+// of them.
 // ------------------------------------------------------------------------------------------
 constexpr int PP_BM = 256;        // query rows per workgroup
 constexpr int PP_NT = 512;        // 8 wavefronts
@@ -159,7 +160,6 @@ __device__ __forceinline__ void phase_qk(RowState<D>& st, const bf16x8 (&qf)[D /
     }
 }
 
-// O^T += V^T P^T for the 64 keys of a tile (four 16-key steps).
 // V^T operands of a matrix phase's first PV products that its wavefront reads at the end of its
 // previous (vector) phase, so that the phase opens with an MFMA instead of an LDS wait (deeper
 // prefetch measured no better)
@@ -177,6 +177,7 @@ __device__ __forceinline__ bf16x8 read_vt0(const char* vbase, int v_row, int v_c
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// O^T += V^T P^T for the 64 keys of a tile (four 16-key steps).
 template <int D>
 __device__ __forceinline__ void phase_pv(RowState<D>& st, const char* vbase, int v_row, int v_col,
                                          const bf16x8 (&av0)[NPRE]) {
