@@ -22,6 +22,8 @@ CASES = [  # name, geometry, (w_f, w_p), planted
     ("wide_p_small", Geometry(1, 3, 40, 2, 2, 128), (1, 1), False),
     ("one_frame", Geometry(1, 3, 1, 12, 20, 64), (1, 6), False),
     ("tail120", Geometry(1, 3, 2, 6, 10, 128), (0, 2), True),
+    ("one_location", Geometry(1, 3, 150, 1, 1, 64), (2, 0), False),
+    ("one_location128", Geometry(1, 3, 300, 1, 1, 128), (1, 3), False),
 ]
 
 

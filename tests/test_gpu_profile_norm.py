@@ -74,17 +74,18 @@ def test_profile_planted_cogvideox_shape(gpu):
 # In-frame positions per key (frames of < 32 tokens, or a band leaving < 20 positions of a frame
 # out) instead of one band interval per tile.  64 heads, so that each key split holds several
 # tiles of 32 keys (the tile buffers rotate); the last split is ragged.
-PER_KEY_CASES = [
-    ("P24_D64", 4, 6, 64, 5),
-    ("P24_D128", 4, 6, 128, 5),
-    ("P36_wide_band", 6, 6, 128, 10),
+PER_KEY_CASES = [  # name, F, HH, WW, D, w_p
+    ("P24_D64", 60, 4, 6, 64, 5),
+    ("P24_D128", 60, 4, 6, 128, 5),
+    ("P36_wide_band", 60, 6, 6, 128, 10),
+    ("P1_one_location", 200, 1, 1, 128, 3),
 ]
 
 
 @pytest.mark.parametrize("case", PER_KEY_CASES, ids=[c[0] for c in PER_KEY_CASES])
 def test_profile_per_key_positions(gpu, case):
-    _, HH, WW, D, w_p = case
-    g = Geometry(1, 64, 60, HH, WW, D)
+    _, F, HH, WW, D, w_p = case
+    g = Geometry(1, 64, F, HH, WW, D)
     note(f"profile per-key positions {case[0]}")
     q, k, v = make_qkv(Workload("perkey", g, 1, w_p, 64, 33, 133, planted=True), device=DEV)
     idx = sample_queries(g.S, 64, 133)
