@@ -7,14 +7,14 @@
 //
 // Pass 1 (split-K): a workgroup of four wavefronts takes one (head, key range, group of 64
 // sampled queries), 16 queries per wavefront, and two workgroups share a CU, so that one's
-// matrix products overlap the other's exponentials.  Per 32-key tile and wavefront, with
+// matrix products overlap the other's exponentials.  Per 64-key tile and wavefront, with
 // v_mfma_f32_16x16x32_bf16 (lane l: row/column l%16, k-quarter l/16):
 //   S^T[key][query] = K Q^T       A = K rows from LDS, B = the wavefront's Q rows, kept in
-//                                 registers; lane l holds 8 scores of query l%16.
+//                                 registers; lane l holds 16 scores of query l%16.
 //   O_x^T[d][query] += V^T P_x^T  for the three softmax states x (dense, spatial, temporal):
 //                                 A = V^T from the LDS transpose read, shared by the three
 //                                 products; B = P_x^T converted to bf16 straight from the
-//                                 score registers (the key order inside the 32-key step is
+//                                 score registers (the key order inside each 32-key step is
 //                                 permuted identically on both operands).
 // The three states share one running reference max, the unmasked one: softmax does not
 // depend on the reference, so each masked state only selects the unmasked exponentials of
@@ -24,7 +24,7 @@
 // temporal mask compares in-frame positions (key mod P).  Each wavefront writes the
 // unnormalised partial state (reference max, row sum, O) of its queries to the workspace.
 // Key and value tiles are copied HBM -> LDS (global_load_lds_dwordx4, no register staging)
-// into four buffers, three tiles ahead of their use.
+// into two buffers, one tile ahead of their use.
 // Pass 2: one workgroup per (head, sampled row) merges that row's partial states with
 // log-sum-exp weights, forms its three outputs (one channel per thread) and sums the two
 // squared errors over the channels in fp64.
@@ -39,8 +39,10 @@ namespace {
 
 constexpr int NT = 256;            // partial pass: four wavefronts
 constexpr int NT_RED = 256;        // reduce pass
-constexpr int TILE = 32;           // keys per tile
-constexpr int NBUF = 4;            // tile buffers (copies run NBUF-1 tiles ahead)
+constexpr int TILE = 64;           // keys per tile
+constexpr int NBUF = 2;            // tile buffers (copies run NBUF-1 tiles ahead)
+constexpr int NKB = TILE / 16;     // 16-key score blocks per tile
+constexpr int NST = TILE / 32;     // 32-key PV steps per tile
 constexpr int QG = 64;             // sampled queries per workgroup
 constexpr int MAX_SPLIT = 128;
 constexpr int TARGET_WGS = 512;    // two workgroups per CU
@@ -130,17 +132,17 @@ __device__ __forceinline__ float add_bf16x8(const bf16x8& p, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 6, 7), one, acc, false);
 }
 
-// Temporal-mask modes.  A lane's keys in a tile are kl + dk, dk in {0..3, 16..19}.
-//   TP_INTERVAL: frames of >= 32 tokens (the lane's keys cross at most one frame boundary) and
-//     a band that leaves >= 20 positions of a frame out (P - 2 w_p - 1 >= 20).  The keys of the
-//     band in the first frame, [lo0, hi0] in dk, and in the next, [lo0 + P, hi0 + P], are then
-//     at least 20 apart, so at most one of them meets the lane's keys: one interval [a, b) of
-//     dk per tile, clipped at the frame boundary.
+// Temporal-mask modes.  A lane's keys in a tile are kl + dk, dk = 16 kb + r (kb < 4, r < 4).
+//   TP_INTERVAL: frames of >= 64 tokens (the lane's keys, a span of 52, cross at most one
+//     frame boundary) and a band that leaves >= 52 positions of a frame out
+//     (P - 2 w_p - 1 >= 52).  The keys of the band in the first frame, [lo0, hi0] in dk, and in
+//     the next, [lo0 + P, hi0 + P], are then at least 52 apart, so at most one of them meets
+//     the lane's keys: one interval [a, b) of dk per tile, clipped at the frame boundary.
 //   TP_PER_KEY: in-frame position of every key by one division.
 constexpr int TP_PER_KEY = 0;
 constexpr int TP_INTERVAL = 1;
 
-// One 32-key tile for one wavefront: scores, masks, softmax, PV products.
+// One 64-key tile for one wavefront: scores, masks, softmax, PV products.
 template <int D, int TPM>
 __device__ __forceinline__ void profile_tile(PState<D>& st, const bf16x8 (&qf)[D / 32], const char* kt, const bf16* vt,
                                              int32_t k0, int32_t ke, float c, int32_t sp_lo, uint32_t sp_span,
@@ -151,13 +153,13 @@ __device__ __forceinline__ void profile_tile(PState<D>& st, const bf16x8 (&qf)[D
   const int g = lane >> 4, i16 = lane & 15;
 
   // ---- S^T = K Q^T: two 16-key blocks ----
-  f32x4 sacc[2];
+  f32x4 sacc[NKB];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int kb = 0; kb < NKB; ++kb) sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < NKB; ++kb) {
       const int r = 16 * kb + i16;
       const bf16x8 ak = *reinterpret_cast<const bf16x8*>(kt + r * T::ROW_BYTES + 16 * ((4 * ks + g) ^ T::swz_k(r)));
       sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, qf[ks], sacc[kb], 0, 0, 0);
@@ -167,7 +169,7 @@ __device__ __forceinline__ void profile_tile(PState<D>& st, const bf16x8 (&qf)[D
   const int32_t kl = k0 + 4 * g;                // key of element (kb, r): kl + 16 kb + r
   if (k0 + TILE > ke) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         if (kl + 16 * kb + r >= ke) sacc[kb][r] = -INFINITY;
@@ -176,7 +178,7 @@ __device__ __forceinline__ void profile_tile(PState<D>& st, const bf16x8 (&qf)[D
   // ---- shared reference max with lazy rescaling of all three states ----
   float mx = -INFINITY;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[kb][r]);
   mx = max_x32(max_x16(mx)) * c;
@@ -208,9 +210,9 @@ __device__ __forceinline__ void profile_tile(PState<D>& st, const bf16x8 (&qf)[D
     const int32_t tp_b = first ? min(hi0 + 1, wth) : hi0 + a.P + 1;
     tp_span = (uint32_t)max(tp_b - tp_a, 0);
   }
-  bf16x8 pb[3];
+  bf16x8 pb[NST][3];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int32_t dk = 16 * kb + r;
@@ -223,31 +225,38 @@ __device__ __forceinline__ void profile_tile(PState<D>& st, const bf16x8 (&qf)[D
       }
       const bool in_sp = (uint32_t)(dk - sp_a) < sp_span;
       const float pr = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], c, -m_use));
-      pb[0][4 * kb + r] = (bf16)pr;
-      pb[1][4 * kb + r] = (bf16)(in_sp ? pr : 0.f);
-      pb[2][4 * kb + r] = (bf16)(in_tp ? pr : 0.f);
+      pb[kb >> 1][0][4 * (kb & 1) + r] = (bf16)pr;
+      pb[kb >> 1][1][4 * (kb & 1) + r] = (bf16)(in_sp ? pr : 0.f);
+      pb[kb >> 1][2][4 * (kb & 1) + r] = (bf16)(in_tp ? pr : 0.f);
     }
   // row sums of the bf16 weights the PV products use
 #pragma unroll
-  for (int x = 0; x < 3; ++x) st.l[x] = add_bf16x8(pb[x], st.l[x]);
+  for (int x = 0; x < 3; ++x)
+#pragma unroll
+    for (int s = 0; s < NST; ++s) st.l[x] = add_bf16x8(pb[s][x], st.l[x]);
 
-  // ---- O_x^T += V^T P_x^T.  The transpose read hands lane i of each 16-lane group column i
-  // of the 4 rows x 16 columns its group addressed: group g reads keys 4g..4g+3 (and, 16 rows
-  // further, 16+4g..16+4g+3), the keys whose scores lane l holds in sacc[0] and sacc[1]. ----
+  // ---- O_x^T += V^T P_x^T, per 32-key step s.  The transpose read hands lane i of each
+  // 16-lane group column i of the 4 rows x 16 columns its group addressed: group g reads keys
+  // 32s+4g..32s+4g+3 (and, 16 rows further, 32s+16+4g..), the keys whose scores lane l holds
+  // in sacc[2s] and sacc[2s+1]. ----
   const int vr = 4 * g + (i16 >> 2);
   const int vc = 4 * (i16 & 3);                 // column inside the 16-channel block
-  const char* v0 = reinterpret_cast<const char*>(vt) + vr * T::ROW_BYTES;
-  const char* v1 = v0 + 16 * T::ROW_BYTES;
-  const int sw0 = T::swz_v(vr), sw1 = T::swz_v(vr + 16);
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    const int col = 16 * db + vc;
-    const int cb = 2 * (col & 7);
-    const i16x4 lo = lds_read_tr(reinterpret_cast<const bf16*>(v0 + 16 * ((col >> 3) ^ sw0) + cb));
-    const i16x4 hi = lds_read_tr(reinterpret_cast<const bf16*>(v1 + 16 * ((col >> 3) ^ sw1) + cb));
-    const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  for (int s = 0; s < NST; ++s) {
+    const char* v0 = reinterpret_cast<const char*>(vt) + (32 * s + vr) * T::ROW_BYTES;
+    const char* v1 = v0 + 16 * T::ROW_BYTES;
+    const int sw0 = T::swz_v(32 * s + vr), sw1 = T::swz_v(32 * s + vr + 16);
 #pragma unroll
-    for (int x = 0; x < 3; ++x) st.o[x][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[x], st.o[x][db], 0, 0, 0);
+    for (int db = 0; db < NDB; ++db) {
+      const int col = 16 * db + vc;
+      const int cb = 2 * (col & 7);
+      const i16x4 lo = lds_read_tr(reinterpret_cast<const bf16*>(v0 + 16 * ((col >> 3) ^ sw0) + cb));
+      const i16x4 hi = lds_read_tr(reinterpret_cast<const bf16*>(v1 + 16 * ((col >> 3) ^ sw1) + cb));
+      const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int x = 0; x < 3; ++x)
+        st.o[x][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[s][x], st.o[x][db], 0, 0, 0);
+    }
   }
 }
 
@@ -258,12 +267,8 @@ __global__ __launch_bounds__(NT, 2) void profile_partial_kernel(ProfileArgs a) {
   constexpr int NDB = D / 16;
   __shared__ __attribute__((aligned(1024))) bf16 K0[TILE * D];
   __shared__ __attribute__((aligned(1024))) bf16 K1[TILE * D];
-  __shared__ __attribute__((aligned(1024))) bf16 K2[TILE * D];
-  __shared__ __attribute__((aligned(1024))) bf16 K3[TILE * D];
   __shared__ __attribute__((aligned(1024))) bf16 V0[TILE * D];
   __shared__ __attribute__((aligned(1024))) bf16 V1[TILE * D];
-  __shared__ __attribute__((aligned(1024))) bf16 V2[TILE * D];
-  __shared__ __attribute__((aligned(1024))) bf16 V3[TILE * D];
 
   int32_t bid = blockIdx.x;
   const int32_t zq = bid % a.n_zq;
@@ -300,10 +305,6 @@ __global__ __launch_bounds__(NT, 2) void profile_partial_kernel(ProfileArgs a) {
   __builtin_amdgcn_sched_barrier(0);
   tile_copy<D>(K, ks, a.S, K0, wave, lane, false);
   tile_copy<D>(V, ks, a.S, V0, wave, lane, true);
-  tile_copy<D>(K, ks + TILE, a.S, K1, wave, lane, false);
-  tile_copy<D>(V, ks + TILE, a.S, V1, wave, lane, true);
-  tile_copy<D>(K, ks + 2 * TILE, a.S, K2, wave, lane, false);
-  tile_copy<D>(V, ks + 2 * TILE, a.S, V2, wave, lane, true);
 
   PState<D> st;
 #pragma unroll
@@ -327,13 +328,9 @@ __global__ __launch_bounds__(NT, 2) void profile_partial_kernel(ProfileArgs a) {
                          (uint32_t)(sp_hi - sp_lo), pq, a, lane);
   };
   for (int32_t t = 0; t < ntiles; t += NBUF) {
-    step(t, K0, V0, K3, V3);
+    step(t, K0, V0, K1, V1);
     if (t + 1 >= ntiles) break;
     step(t + 1, K1, V1, K0, V0);
-    if (t + 2 >= ntiles) break;
-    step(t + 2, K2, V2, K1, V1);
-    if (t + 3 >= ntiles) break;
-    step(t + 3, K3, V3, K2, V2);
   }
   __builtin_amdgcn_s_waitcnt(VMCNT0);
 
@@ -473,8 +470,8 @@ hipError_t launch_profile(const ProfileArgs& a, hipStream_t st) {
   const dim3 g1((unsigned)((int64_t)a.BH * a.nsplit * a.n_zq));
   const dim3 g2((unsigned)((int64_t)a.BH * a.n_q));
   const dim3 g3((unsigned)a.BH);
-  // the band test per tile needs frames of >= 32 tokens and >= 20 positions outside the band
-  const bool interval = a.P >= 32 && (int64_t)a.P - 2 * (int64_t)a.w_p - 1 >= 20;
+  // the band test per tile needs frames of >= 64 tokens and >= 52 positions outside the band
+  const bool interval = a.P >= 64 && (int64_t)a.P - 2 * (int64_t)a.w_p - 1 >= 52;
   if (a.D == 128) {
     if (interval) profile_partial_kernel<128, TP_INTERVAL><<<g1, NT, 0, st>>>(a);
     else profile_partial_kernel<128, TP_PER_KEY><<<g1, NT, 0, st>>>(a);

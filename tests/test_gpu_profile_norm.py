@@ -71,13 +71,13 @@ def test_profile_planted_cogvideox_shape(gpu):
     _check_profile(gpu, q, k, v, idx, g, wl.w_f, wl.w_p, expect=expected_planted_kinds(wl), what="cogvideox")
 
 
-# In-frame positions per key (frames of < 32 tokens, or a band leaving < 20 positions of a frame
+# In-frame positions per key (frames of < 64 tokens, or a band leaving < 52 positions of a frame
 # out) instead of one band interval per tile.  64 heads, so that each key split holds several
-# tiles of 32 keys (the tile buffers rotate); the last split is ragged.
+# tiles of 64 keys (the two tile buffers alternate); the last split is ragged.
 PER_KEY_CASES = [  # name, F, HH, WW, D, w_p
     ("P24_D64", 60, 4, 6, 64, 5),
     ("P24_D128", 60, 4, 6, 128, 5),
-    ("P36_wide_band", 60, 6, 6, 128, 10),
+    ("P80_wide_band", 60, 8, 10, 128, 20),
     ("P1_one_location", 200, 1, 1, 128, 3),
 ]
 
