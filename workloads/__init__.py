@@ -153,3 +153,83 @@ def expected_planted_kinds(wl: Workload, layer: int = 0) -> Optional[np.ndarray]
 def bf16_to_f64(t: torch.Tensor) -> np.ndarray:
     """Exact widening of a bf16 (or fp32) tensor to a float64 numpy array."""
     return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+# ----------------------------------------------------------------------------------------------
+# Semantic workloads (Sparse VideoGen2): tokens carry a hidden semantic class
+# ----------------------------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class SemanticWorkload:
+    """Q/K/V whose rows belong to hidden semantic classes, for the clustering path.
+
+    Every token gets one of `n_classes` classes from a seeded map of coarse
+    image regions (blocks of `region` rows x columns) that is redrawn every
+    `frames_per_draw` frames, so a class is a set of scattered patches, as an
+    object's tokens are.  Q and K rows of class z are N(0, I) plus `strength`
+    times one shared random vector of (head, z); V is N(0, I).
+    """
+    name: str
+    geom: Geometry
+    n_classes: int
+    strength: float
+    Cq: int               # query clusters
+    Ck: int               # key clusters
+    p: float              # top-p threshold
+    iters: int            # k-means iterations of one call
+    seed: int
+    region: int = 5
+    frames_per_draw: int = 4
+
+
+SEMANTIC_WORKLOADS: Dict[str, SemanticWorkload] = {
+    # small enough for the oracle in full
+    "svg2_small": SemanticWorkload("svg2_small", Geometry(1, 2, 4, 8, 10, 64), 4, 0.8, 8, 16, 0.9, 4, 21,
+                                   region=3, frames_per_draw=2),
+    # the 720p token grid of the spatial/temporal workloads
+    "hunyuan720p_svg2": SemanticWorkload("hunyuan720p_svg2", Geometry(1, 24, 33, 45, 80, 128), 8, 0.8, 128, 512,
+                                         0.9, 3, 22),
+}
+
+
+def semantic_classes(wl: SemanticWorkload) -> np.ndarray:
+    """int64 [H, S]: hidden class of every frame-major token of each head."""
+    g = wl.geom
+    rng = np.random.default_rng(wl.seed + 4099)
+    nfd = -(-g.F // wl.frames_per_draw)
+    ny, nx = -(-g.HH // wl.region), -(-g.WW // wl.region)
+    draw = rng.integers(0, wl.n_classes, size=(g.H, nfd, ny, nx))
+    f = np.arange(g.F) // wl.frames_per_draw
+    y = np.arange(g.HH) // wl.region
+    x = np.arange(g.WW) // wl.region
+    z = draw[:, f[:, None, None], y[None, :, None], x[None, None, :]]
+    return z.reshape(g.H, g.S).astype(np.int64)
+
+
+def make_qkv_semantic(wl: SemanticWorkload, device: str = "cpu", step: int = 0, dtype=torch.bfloat16):
+    """Q, K, V [B, H, S, D] (bf16 by default) with the hidden classes of semantic_classes().
+
+    `step` redraws the noise (a later denoising step) while the classes and their
+    vectors stay, so that centroids of one step are a warm start for the next.
+    """
+    g = wl.geom
+    gen = torch.Generator(device=device)
+    gen.manual_seed(wl.seed * 1000)
+    mu = torch.randn((g.H, wl.n_classes, g.D), generator=gen, device=device, dtype=torch.float32)
+    gen.manual_seed(wl.seed * 1000 + 1 + step)
+    shape = (g.B, g.H, g.S, g.D)
+    q = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    k = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    v = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    z = torch.from_numpy(semantic_classes(wl)).to(device)
+    for h in range(g.H):
+        add = wl.strength * mu[h][z[h]]
+        q[:, h] += add
+        k[:, h] += add
+        del add
+    return q.to(dtype), k.to(dtype), v.to(dtype)
+
+
+def init_token_indices(S: int, C: int, seed: int) -> np.ndarray:
+    """C distinct token indices of [0, S) (int32, sorted) whose rows start a cold k-means."""
+    rng = np.random.default_rng(seed + 7)
+    return np.sort(rng.choice(S, size=C, replace=False)).astype(np.int32)
