@@ -58,6 +58,8 @@ typedef int32_t svg_status;
 #define SVG_OP_PROFILE     1
 #define SVG_OP_SPARSE_ATTN 2
 #define SVG_OP_LAYER       3
+#define SVG_OP_KMEANS      4   /* n = cluster count C */
+#define SVG_OP_CLUSTER_ATTN 5  /* n = query cluster count Cq */
 
 typedef struct {
     int32_t B, H;       /* batch, heads */
@@ -201,8 +203,85 @@ svg_status svg_layer(const void* q, const void* k, const void* v, const float* w
  */
 int32_t svg_dense_step(int32_t step, int32_t n_steps, float dense_fraction);
 
-/* Bytes of workspace a call needs (0 for an invalid request). */
-size_t svg_workspace_bytes(int32_t op, const svg_geom* g, int32_t n_q);
+/*
+ * ---------------------------------------------------------------------------------------
+ * Semantic clustering path ([svg2-gist] technical summary, section 2: A semantic-aware
+ * permutation, B centroid-based top-p selection, C centroid cache and a kernel for
+ * variable-size blocks).  Per (b, h): cluster the Q rows into Cq clusters and the K rows
+ * into Ck clusters (svg_kmeans, twice), pick per query cluster the key clusters that carry
+ * the top-p share of its estimated attention (svg_centroid_topp), and attend each query to
+ * exactly the keys of its selected clusters (svg_cluster_attn).
+ * ---------------------------------------------------------------------------------------
+ */
+
+/*
+ * svg_kmeans -- `iters` Lloyd iterations on the rows of x (section 2A): every row goes to the
+ * nearest centroid (squared Euclidean distance to the centroid rounded to bf16, evaluated as
+ * bf16 products with fp32 accumulation; ties to the lowest index), then every centroid moves to
+ * the fp64 mean of its rows, rounded to fp32; an empty cluster keeps its centroid.
+ *
+ * x:          bf16 [B][H][S][D] (Q or K), read only.
+ * C:          clusters per (b, h), 1 <= C <= min(S, 4096).   iters: 1 .. 1000.
+ * init_idx:   int32 [C] token indices or NULL.  Given: a cold start -- centroid c of every
+ *             (b, h) starts as the row at token init_idx[c] (indices are clamped into [0, S)).
+ *             NULL: start from the centroids passed in (the previous denoising step's, the
+ *             cache of section 2C).
+ * centroids:  fp32 [B*H][C][D], in (unless init_idx) and out: the centroids of the last update.
+ * labels:     int32 [B*H][S] out: cluster of each token at the last assignment (so every
+ *             centroid is the mean of the rows labelled with it).
+ * perm:       int32 [B*H][S] out: the tokens sorted by cluster, stably (clusters in index
+ *             order, tokens in order inside a cluster) -- the permutation of section 2A.
+ * offsets:    int32 [B*H][C+1] out: cluster c holds perm[offsets[c] .. offsets[c+1]).
+ * ws:         >= svg_workspace_bytes(SVG_OP_KMEANS, &g, C) bytes.
+ */
+svg_status svg_kmeans(const void* x, svg_geom g, int32_t C, int32_t iters, const int32_t* init_idx,
+                      float* centroids, int32_t* labels, int32_t* perm, int32_t* offsets, void* ws, size_t ws_bytes,
+                      void* stream);
+
+/*
+ * svg_centroid_topp -- centroid-based top-p selection (section 2B), in fp64.  For query
+ * cluster i and key cluster j with n_j > 0 keys, s_ij = scale * cq_i . ck_j and the estimated
+ * share of i's attention on j is w_ij = n_j exp(s_ij) / sum_j' n_j' exp(s_ij') (a centroid
+ * stands for all n_j keys of its cluster; empty clusters get 0).  Per query cluster, key
+ * clusters are taken in decreasing w (ties: lower index first) until the taken shares sum to
+ * at least p; clusters of share 0 are never taken.
+ *
+ * cq, ck:     fp32 [B*H][Cq][D], [B*H][Ck][D] (svg_kmeans centroids of Q and of K).
+ * k_offsets:  int32 [B*H][Ck+1] from svg_kmeans of K (cluster sizes n_j).
+ * Cq:         1 .. S.   Ck: 1 .. min(S, 1024).   p: (0, 1].   scale > 0.
+ * sel:        uint8 [B*H][Cq][Ck] out: 1 for a selected key cluster.  Every query cluster
+ *             selects at least one non-empty key cluster.
+ */
+svg_status svg_centroid_topp(const float* cq, const float* ck, const int32_t* k_offsets, svg_geom g, int32_t Cq,
+                             int32_t Ck, float scale, float p, uint8_t* sel, void* stream);
+
+/*
+ * svg_cluster_attn -- attention over the selected clusters (sections 2A and 2C): every query
+ * token attends exactly to the keys of the key clusters selected for its query cluster,
+ * softmax(scale q k^T) v with bf16 products, fp32 accumulation and online softmax (the
+ * weights rounded to bf16 for the value product).  The queries of one cluster are computed
+ * together as dense tiles of up to 256 rows; their keys are gathered row by row from the key
+ * list (the sorted tokens of the selected key clusters), so no tile is padded with keys of
+ * unselected clusters.
+ *
+ * q, k, v:    bf16 [B][H][S][D] frame-major (the model's order), read only.
+ * q_perm, q_offsets, k_perm, k_offsets: svg_kmeans outputs for Q (Cq clusters) and K (Ck).
+ * sel:        uint8 [B*H][Cq][Ck] from svg_centroid_topp.
+ * Cq:         1 .. min(S, 32767).   Ck: 1 .. min(S, 1024).   S <= 65535 * 256.
+ * o:          bf16 [B][H][S][D] out, in the original token order.  A query cluster whose
+ *             selected clusters hold no key leaves its rows unwritten (svg_centroid_topp never
+ *             produces one).
+ * ws:         >= svg_workspace_bytes(SVG_OP_CLUSTER_ATTN, &g, Cq) bytes (the key lists:
+ *             B*H*Cq*S int32, plus work items).
+ */
+svg_status svg_cluster_attn(const void* q, const void* k, const void* v, const int32_t* q_perm,
+                            const int32_t* q_offsets, const int32_t* k_perm, const int32_t* k_offsets,
+                            const uint8_t* sel, svg_geom g, int32_t Cq, int32_t Ck, float scale, void* o, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/* Bytes of workspace a call needs (0 for an invalid request); n is the sample size n_q for
+ * SVG_OP_PROFILE and SVG_OP_LAYER, the cluster count for SVG_OP_KMEANS and SVG_OP_CLUSTER_ATTN. */
+size_t svg_workspace_bytes(int32_t op, const svg_geom* g, int32_t n);
 
 /* Query-block x key-block tile of svg_sparse_attn / svg_dense_attn. */
 void svg_tile_shape(int32_t* bm, int32_t* bn);

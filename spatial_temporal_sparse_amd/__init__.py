@@ -26,6 +26,8 @@ DENSE = 2
 OP_PROFILE = 1
 OP_SPARSE_ATTN = 2
 OP_LAYER = 3
+OP_KMEANS = 4
+OP_CLUSTER_ATTN = 5
 
 _c_i32 = ctypes.c_int32
 _c_vp = ctypes.c_void_p
@@ -45,32 +47,41 @@ class SvgError(RuntimeError):
         self.status = status
 
 
+_st = _c_i32
+# result and argument types of every exported call
+_SIGNATURES = {
+    "svg_qknorm_rope": (_st, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, ctypes.c_float, ctypes.c_float,
+                             _c_i32, _c_i32, _c_i32, Geom, _c_vp]),
+    "svg_profile_heads": (_st, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, Geom, Windows, ctypes.c_float, _c_vp, _c_vp,
+                               _c_vp, ctypes.c_size_t, _c_vp]),
+    "svg_permute": (_st, [_c_vp, _c_vp, _c_i32, _c_vp, _c_i32, Geom, _c_vp]),
+    "svg_unpermute": (_st, [_c_vp, _c_vp, _c_i32, _c_vp, _c_i32, Geom, _c_vp]),
+    "svg_build_block_mask": (_st, [_c_vp, Geom, Windows, _c_i32, _c_i32, _c_vp, _c_vp]),
+    "svg_sparse_attn": (_st, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, Geom, Windows, ctypes.c_float,
+                             _c_vp, _c_vp, _c_vp, ctypes.c_size_t, _c_vp]),
+    "svg_dense_attn": (_st, [_c_vp, _c_vp, _c_vp, Geom, ctypes.c_float, _c_vp, _c_vp]),
+    "svg_layer": (_st, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, ctypes.c_float, ctypes.c_float, _c_i32, _c_i32, _c_i32,
+                       _c_vp, _c_vp, _c_vp, _c_i32, Geom, Windows, ctypes.c_float, _c_i32, _c_vp, _c_vp, _c_vp,
+                       _c_vp, ctypes.c_size_t, _c_vp]),
+    "svg_dense_step": (_c_i32, [_c_i32, _c_i32, ctypes.c_float]),
+    "svg_kmeans": (_st, [_c_vp, Geom, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, ctypes.c_size_t,
+                        _c_vp]),
+    "svg_centroid_topp": (_st, [_c_vp, _c_vp, _c_vp, Geom, _c_i32, _c_i32, ctypes.c_float, ctypes.c_float, _c_vp,
+                               _c_vp]),
+    "svg_cluster_attn": (_st, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, Geom, _c_i32, _c_i32,
+                              ctypes.c_float, _c_vp, _c_vp, ctypes.c_size_t, _c_vp]),
+    "svg_workspace_bytes": (ctypes.c_size_t, [_c_i32, ctypes.POINTER(Geom), _c_i32]),
+    "svg_tile_shape": (None, [ctypes.POINTER(_c_i32), ctypes.POINTER(_c_i32)]),
+    "svg_status_string": (ctypes.c_char_p, [_c_i32]),
+    "svg_last_error": (ctypes.c_char_p, []),
+}
+
+
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python {os.path.join(_HERE, 'build.py')}`")
     lib = ctypes.CDLL(LIB_PATH)
-    st = _c_i32
-    sig = {
-        "svg_qknorm_rope": (st, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, ctypes.c_float, ctypes.c_float,
-                                 _c_i32, _c_i32, _c_i32, Geom, _c_vp]),
-        "svg_profile_heads": (st, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, Geom, Windows, ctypes.c_float, _c_vp, _c_vp,
-                                   _c_vp, ctypes.c_size_t, _c_vp]),
-        "svg_permute": (st, [_c_vp, _c_vp, _c_i32, _c_vp, _c_i32, Geom, _c_vp]),
-        "svg_unpermute": (st, [_c_vp, _c_vp, _c_i32, _c_vp, _c_i32, Geom, _c_vp]),
-        "svg_build_block_mask": (st, [_c_vp, Geom, Windows, _c_i32, _c_i32, _c_vp, _c_vp]),
-        "svg_sparse_attn": (st, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, Geom, Windows, ctypes.c_float,
-                                 _c_vp, _c_vp, _c_vp, ctypes.c_size_t, _c_vp]),
-        "svg_dense_attn": (st, [_c_vp, _c_vp, _c_vp, Geom, ctypes.c_float, _c_vp, _c_vp]),
-        "svg_layer": (st, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, ctypes.c_float, ctypes.c_float, _c_i32, _c_i32, _c_i32,
-                           _c_vp, _c_vp, _c_vp, _c_i32, Geom, Windows, ctypes.c_float, _c_i32, _c_vp, _c_vp, _c_vp,
-                           _c_vp, ctypes.c_size_t, _c_vp]),
-        "svg_dense_step": (_c_i32, [_c_i32, _c_i32, ctypes.c_float]),
-        "svg_workspace_bytes": (ctypes.c_size_t, [_c_i32, ctypes.POINTER(Geom), _c_i32]),
-        "svg_tile_shape": (None, [ctypes.POINTER(_c_i32), ctypes.POINTER(_c_i32)]),
-        "svg_status_string": (ctypes.c_char_p, [_c_i32]),
-        "svg_last_error": (ctypes.c_char_p, []),
-    }
-    for name, (res, args) in sig.items():
+    for name, (res, args) in _SIGNATURES.items():
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
@@ -416,3 +427,130 @@ class StepDriver:
             self._graph[dense] = g
         g.replay()
         return self.o, self.kind, self.mse
+
+
+# ----------------------------------------------------------------------------------------------
+# Semantic clustering path (Sparse VideoGen2)
+# ----------------------------------------------------------------------------------------------
+class Clusters:
+    """Output of kmeans(): centroids [B, H, C, D] fp32, labels / perm [B, H, S] int32 and
+    offsets [B, H, C + 1] int32 (cluster c holds perm[..., offsets[c]:offsets[c + 1]])."""
+
+    def __init__(self, centroids, labels, perm, offsets):
+        self.centroids, self.labels, self.perm, self.offsets = centroids, labels, perm, offsets
+
+    @property
+    def C(self) -> int:
+        return self.centroids.shape[2]
+
+
+def kmeans(x, F, HH, WW, C, iters, init_idx=None, centroids=None, out: Optional[Clusters] = None, ws=None):
+    """Lloyd k-means of the rows of x per (b, h) (svg_kmeans).
+
+    Cold start from the rows at init_idx (int32 [C] device tensor), or a warm start from
+    `centroids` (fp32 [B, H, C, D], updated in place) or from out.centroids.  Returns a
+    Clusters (out, if given).
+    """
+    g = geometry(x, F, HH, WW)
+    _check_qkv("x", x, _shape(g))
+    dev = x.device
+    S = g.F * g.HH * g.WW
+    if init_idx is None and centroids is None and out is None:
+        raise ValueError("kmeans needs init_idx (cold start), centroids or out (warm start)")
+    if out is None:
+        cent = centroids if centroids is not None else torch.empty((g.B, g.H, C, g.D), dtype=torch.float32, device=dev)
+        out = Clusters(cent, torch.empty((g.B, g.H, S), dtype=torch.int32, device=dev),
+                       torch.empty((g.B, g.H, S), dtype=torch.int32, device=dev),
+                       torch.empty((g.B, g.H, C + 1), dtype=torch.int32, device=dev))
+    elif centroids is not None and centroids.data_ptr() != out.centroids.data_ptr():
+        out.centroids.copy_(centroids)
+    _check_qkv("centroids", out.centroids, (g.B, g.H, C, g.D), torch.float32, dev)
+    _check_qkv("labels", out.labels, (g.B, g.H, S), torch.int32, dev)
+    _check_qkv("perm", out.perm, (g.B, g.H, S), torch.int32, dev)
+    _check_qkv("offsets", out.offsets, (g.B, g.H, C + 1), torch.int32, dev)
+    if init_idx is not None:
+        _check_qkv("init_idx", init_idx, (C,), torch.int32, dev)
+    ws = _workspace(OP_KMEANS, g, C, dev, ws)
+    _check(lib.svg_kmeans(_ptr(x), g, C, iters, _ptr(init_idx), _ptr(out.centroids), _ptr(out.labels), _ptr(out.perm),
+                          _ptr(out.offsets), _ptr(ws), ws.numel(), _stream(x)))
+    return out
+
+
+def centroid_topp(cq: Clusters, ck: Clusters, F, HH, WW, p, scale=None, sel=None):
+    """Key clusters selected per query cluster (svg_centroid_topp): uint8 [B, H, Cq, Ck]."""
+    B, H, Cq, D = cq.centroids.shape
+    Ck = ck.C
+    g = Geom(B, H, F, HH, WW, D)
+    dev = cq.centroids.device
+    _check_qkv("ck.centroids", ck.centroids, (B, H, Ck, D), torch.float32, dev)
+    _check_qkv("ck.offsets", ck.offsets, (B, H, Ck + 1), torch.int32, dev)
+    sel = torch.empty((B, H, Cq, Ck), dtype=torch.uint8, device=dev) if sel is None else sel
+    _check_qkv("sel", sel, (B, H, Cq, Ck), torch.uint8, dev)
+    sc = default_scale(D) if scale is None else scale
+    _check(lib.svg_centroid_topp(_ptr(cq.centroids), _ptr(ck.centroids), _ptr(ck.offsets), g, Cq, Ck, float(sc),
+                                 float(p), _ptr(sel), _stream(cq.centroids)))
+    return sel
+
+
+def cluster_attn(q, k, v, cq: Clusters, ck: Clusters, sel, F, HH, WW, scale=None, o=None, ws=None):
+    """Attention of every query to the keys of its query cluster's selected key clusters
+    (svg_cluster_attn).  Returns o [B, H, S, D] bf16 in the original token order."""
+    g = geometry(q, F, HH, WW)
+    shp = _shape(g)
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check_qkv(n, t, shp, device=q.device)
+    dev = q.device
+    Cq, Ck = cq.C, ck.C
+    S = shp[2]
+    for n, t, sh in (("cq.perm", cq.perm, (g.B, g.H, S)), ("cq.offsets", cq.offsets, (g.B, g.H, Cq + 1)),
+                     ("ck.perm", ck.perm, (g.B, g.H, S)), ("ck.offsets", ck.offsets, (g.B, g.H, Ck + 1))):
+        _check_qkv(n, t, sh, torch.int32, dev)
+    _check_qkv("sel", sel, (g.B, g.H, Cq, Ck), torch.uint8, dev)
+    o = torch.empty_like(q) if o is None else o
+    _check_qkv("o", o, shp, device=dev)
+    ws = _workspace(OP_CLUSTER_ATTN, g, Cq, dev, ws)
+    sc = default_scale(g.D) if scale is None else scale
+    _check(lib.svg_cluster_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(cq.perm), _ptr(cq.offsets), _ptr(ck.perm),
+                                _ptr(ck.offsets), _ptr(sel), g, Cq, Ck, float(sc), _ptr(o), _ptr(ws), ws.numel(),
+                                _stream(q)))
+    return o
+
+
+class ClusterLayer:
+    """One attention layer of the clustering path with its centroid cache.
+
+    The first call clusters from the rows at the given token indices (a cold start); later
+    calls start k-means from the previous call's centroids, the cache that carries from one
+    denoising step to the next.  Buffers are allocated once.
+    """
+
+    def __init__(self, like: torch.Tensor, F, HH, WW, Cq, Ck, p, iters, init_q, init_k, scale=None):
+        g = geometry(like, F, HH, WW)
+        self.g, self.F, self.HH, self.WW = g, F, HH, WW
+        self.Cq, self.Ck, self.p, self.iters = Cq, Ck, p, iters
+        self.init_q, self.init_k = init_q, init_k
+        self.scale = default_scale(g.D) if scale is None else scale
+        dev = like.device
+        S = F * HH * WW
+        mk = lambda C: Clusters(torch.empty((g.B, g.H, C, g.D), dtype=torch.float32, device=dev),
+                                torch.empty((g.B, g.H, S), dtype=torch.int32, device=dev),
+                                torch.empty((g.B, g.H, S), dtype=torch.int32, device=dev),
+                                torch.empty((g.B, g.H, C + 1), dtype=torch.int32, device=dev))
+        self.cq, self.ck = mk(Cq), mk(Ck)
+        self.sel = torch.empty((g.B, g.H, Cq, Ck), dtype=torch.uint8, device=dev)
+        self.o = torch.empty_like(like)
+        self.ws_km = torch.empty(max(256, workspace_bytes(OP_KMEANS, g, max(Cq, Ck))), dtype=torch.uint8, device=dev)
+        self.ws_attn = torch.empty(max(256, workspace_bytes(OP_CLUSTER_ATTN, g, Cq)), dtype=torch.uint8, device=dev)
+        self.warm = False
+
+    def __call__(self, q, k, v):
+        iq = None if self.warm else self.init_q
+        ik = None if self.warm else self.init_k
+        kmeans(q, self.F, self.HH, self.WW, self.Cq, self.iters, init_idx=iq, out=self.cq, ws=self.ws_km)
+        kmeans(k, self.F, self.HH, self.WW, self.Ck, self.iters, init_idx=ik, out=self.ck, ws=self.ws_km)
+        centroid_topp(self.cq, self.ck, self.F, self.HH, self.WW, self.p, self.scale, sel=self.sel)
+        cluster_attn(q, k, v, self.cq, self.ck, self.sel, self.F, self.HH, self.WW, self.scale, o=self.o,
+                     ws=self.ws_attn)
+        self.warm = True
+        return self.o
+

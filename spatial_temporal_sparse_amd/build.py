@@ -17,7 +17,8 @@ CSRC = os.path.join(HERE, "csrc")
 OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsvg.so")
 
-SOURCES = ["api.cpp", "permute.hip", "block_mask.hip", "qknorm_rope.hip", "attn_fwd.hip", "profile_heads.hip"]
+SOURCES = ["api.cpp", "permute.hip", "block_mask.hip", "qknorm_rope.hip", "attn_fwd.hip", "profile_heads.hip",
+           "cluster.hip"]
 
 ARCH = "gfx950"
 # Packed fp32 VALU forms are disabled for every HIP source on purpose.

@@ -374,6 +374,170 @@ SVG_API svg_status svg_layer(const void* q, const void* k, const void* v, const 
   return SVG_OK;
 }
 
+// ---------------------------------------------------------------------------------------------
+// Semantic clustering path
+// ---------------------------------------------------------------------------------------------
+namespace {
+
+constexpr int32_t KMEANS_MAX_C = 4096;
+constexpr int32_t KMEANS_MAX_ITERS = 1000;
+constexpr int32_t CLUSTER_MAX_CQ = 32767;      // work items hold the query cluster in 15 bits
+
+int32_t geom_S(const svg_geom& g) { return g.F * g.HH * g.WW; }
+
+struct KmeansWs {
+  size_t cb, hn, counts, total;
+};
+KmeansWs kmeans_ws(const svg_geom& g, int32_t C) {
+  const size_t BH = (size_t)g.B * g.H;
+  const size_t Cpad = (size_t)svg::kmeans_cpad(C);
+  KmeansWs w;
+  w.cb = 0;
+  w.hn = w.cb + align_up(BH * Cpad * g.D * 2, 256);
+  w.counts = w.hn + align_up(BH * Cpad * sizeof(float), 256);
+  w.total = w.counts + align_up(BH * (size_t)svg::cluster_nchunk(geom_S(g)) * C * sizeof(int32_t), 256);
+  return w;
+}
+
+struct ClusterWs {
+  size_t klist, klen, items, total;
+};
+ClusterWs cluster_ws(const svg_geom& g, int32_t Cq) {
+  const size_t BH = (size_t)g.B * g.H;
+  const size_t S = (size_t)geom_S(g);
+  ClusterWs w;
+  w.klist = 0;
+  w.klen = align_up(BH * Cq * S * sizeof(int32_t), 256);
+  w.items = w.klen + align_up(BH * Cq * sizeof(int32_t), 256);
+  w.total = w.items + align_up(BH * (size_t)svg::cluster_items_per_head((int32_t)S, Cq) * sizeof(int32_t), 256);
+  return w;
+}
+
+svg_status check_ws(const void* ws, size_t ws_bytes, size_t need, const char* what) {
+  if (ws == nullptr || ws_bytes < need)
+    return fail(SVG_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", what, ws == nullptr ? 0 : ws_bytes,
+                need);
+  if (!aligned16(ws)) return fail(SVG_ERR_INVALID, "%s: workspace is not 16-byte aligned", what);
+  return SVG_OK;
+}
+
+}  // namespace
+
+SVG_API svg_status svg_kmeans(const void* x, svg_geom g, int32_t C, int32_t iters, const int32_t* init_idx,
+                              float* centroids, int32_t* labels, int32_t* perm, int32_t* offsets, void* ws,
+                              size_t ws_bytes, void* stream) {
+  svg_status s;
+  if ((s = check_geom(g, true)) != SVG_OK) return s;
+  if ((s = check_ptrs({{x, "x"}, {centroids, "centroids"}, {labels, "labels"}, {perm, "perm"}, {offsets, "offsets"}})) !=
+      SVG_OK)
+    return s;
+  const int32_t S = geom_S(g);
+  if (C < 1 || C > S || C > KMEANS_MAX_C)
+    return fail(SVG_ERR_INVALID, "cluster count C=%d must lie in [1, min(S=%d, %d)]", C, S, KMEANS_MAX_C);
+  if (iters < 1 || iters > KMEANS_MAX_ITERS)
+    return fail(SVG_ERR_INVALID, "iters=%d must lie in [1, %d]", iters, KMEANS_MAX_ITERS);
+  const KmeansWs w = kmeans_ws(g, C);
+  if ((s = check_ws(ws, ws_bytes, w.total, "svg_kmeans")) != SVG_OK) return s;
+  svg::KmeansArgs a;
+  a.x = (const svg::bf16*)x;
+  a.init_idx = init_idx;
+  a.cent = centroids;
+  a.labels = labels;
+  a.perm = perm;
+  a.offsets = offsets;
+  a.cb = (svg::bf16*)((char*)ws + w.cb);
+  a.hn = (float*)((char*)ws + w.hn);
+  a.counts = (int32_t*)((char*)ws + w.counts);
+  a.BH = g.B * g.H;
+  a.S = S;
+  a.D = g.D;
+  a.C = C;
+  a.iters = iters;
+  return hip_status(svg::launch_kmeans(a, (hipStream_t)stream), "svg_kmeans");
+}
+
+SVG_API svg_status svg_centroid_topp(const float* cq, const float* ck, const int32_t* k_offsets, svg_geom g,
+                                     int32_t Cq, int32_t Ck, float scale, float p, uint8_t* sel, void* stream) {
+  svg_status s;
+  if ((s = check_geom(g, true)) != SVG_OK) return s;
+  if ((s = check_ptrs({{cq, "cq"}, {ck, "ck"}, {k_offsets, "k_offsets"}, {sel, "sel"}})) != SVG_OK) return s;
+  const int32_t S = geom_S(g);
+  if (Cq < 1 || Cq > S) return fail(SVG_ERR_INVALID, "query cluster count Cq=%d must lie in [1, S=%d]", Cq, S);
+  if (Ck < 1 || Ck > S || Ck > svg::TOPP_MAX_CK)
+    return fail(SVG_ERR_INVALID, "key cluster count Ck=%d must lie in [1, min(S=%d, %d)]", Ck, S, svg::TOPP_MAX_CK);
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(SVG_ERR_INVALID, "scale must be finite and > 0");
+  if (!(p > 0.f && p <= 1.f)) return fail(SVG_ERR_INVALID, "p=%g must lie in (0, 1]", (double)p);
+  svg::ToppArgs a;
+  a.cq = cq;
+  a.ck = ck;
+  a.k_off = k_offsets;
+  a.sel = sel;
+  a.BH = g.B * g.H;
+  a.Cq = Cq;
+  a.Ck = Ck;
+  a.D = g.D;
+  a.scale = (double)scale;
+  a.p = (double)p;
+  return hip_status(svg::launch_centroid_topp(a, (hipStream_t)stream), "svg_centroid_topp");
+}
+
+SVG_API svg_status svg_cluster_attn(const void* q, const void* k, const void* v, const int32_t* q_perm,
+                                    const int32_t* q_offsets, const int32_t* k_perm, const int32_t* k_offsets,
+                                    const uint8_t* sel, svg_geom g, int32_t Cq, int32_t Ck, float scale, void* o,
+                                    void* ws, size_t ws_bytes, void* stream) {
+  svg_status s;
+  if ((s = check_geom(g, true)) != SVG_OK) return s;
+  if ((s = check_ptrs({{q, "q"}, {k, "k"}, {v, "v"}, {q_perm, "q_perm"}, {q_offsets, "q_offsets"}, {k_perm, "k_perm"},
+                       {k_offsets, "k_offsets"}, {sel, "sel"}, {o, "o"}})) != SVG_OK)
+    return s;
+  if ((s = check_head_bytes(g)) != SVG_OK) return s;
+  const int32_t S = geom_S(g);
+  if (Cq < 1 || Cq > S || Cq > CLUSTER_MAX_CQ)
+    return fail(SVG_ERR_INVALID, "query cluster count Cq=%d must lie in [1, min(S=%d, %d)]", Cq, S, CLUSTER_MAX_CQ);
+  if (Ck < 1 || Ck > S || Ck > svg::TOPP_MAX_CK)
+    return fail(SVG_ERR_INVALID, "key cluster count Ck=%d must lie in [1, min(S=%d, %d)]", Ck, S, svg::TOPP_MAX_CK);
+  if ((int64_t)S > (int64_t)65535 * svg::CLUSTER_TILE_ROWS)
+    return fail(SVG_ERR_UNSUPPORTED, "S=%d: a query cluster may span more than 65535 tiles", S);
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(SVG_ERR_INVALID, "scale must be finite and > 0");
+  const ClusterWs w = cluster_ws(g, Cq);
+  if ((s = check_ws(ws, ws_bytes, w.total, "svg_cluster_attn")) != SVG_OK) return s;
+  const int32_t BH = g.B * g.H;
+  const int32_t per_head = svg::cluster_items_per_head(S, Cq);
+  svg::ClusterListArgs l;
+  l.sel = sel;
+  l.k_perm = k_perm;
+  l.k_off = k_offsets;
+  l.q_off = q_offsets;
+  l.klist = (int32_t*)((char*)ws + w.klist);
+  l.klen = (int32_t*)((char*)ws + w.klen);
+  l.items = (int32_t*)((char*)ws + w.items);
+  l.BH = BH;
+  l.S = S;
+  l.Cq = Cq;
+  l.Ck = Ck;
+  l.items_per_head = per_head;
+  l.tile_rows = svg::CLUSTER_TILE_ROWS;
+  if ((s = hip_status(svg::launch_cluster_lists(l, (hipStream_t)stream), "svg_cluster_attn (key lists)")) != SVG_OK)
+    return s;
+  svg::ClusterAttnArgs a;
+  a.q = (const svg::bf16*)q;
+  a.k = (const svg::bf16*)k;
+  a.v = (const svg::bf16*)v;
+  a.o = (svg::bf16*)o;
+  a.q_perm = q_perm;
+  a.q_off = q_offsets;
+  a.klist = l.klist;
+  a.klen = l.klen;
+  a.items = l.items;
+  a.BH = BH;
+  a.S = S;
+  a.D = g.D;
+  a.Cq = Cq;
+  a.items_per_head = per_head;
+  a.scale = scale;
+  return hip_status(svg::launch_cluster_attention(a, (hipStream_t)stream), "svg_cluster_attn");
+}
+
 SVG_API size_t svg_workspace_bytes(int32_t op, const svg_geom* g, int32_t n_q) {
   if (g == nullptr) return 0;
   const bool need_d = true;
@@ -391,6 +555,16 @@ SVG_API size_t svg_workspace_bytes(int32_t op, const svg_geom* g, int32_t n_q) {
     const int32_t S = g->F * g->HH * g->WW;
     if (n_q < 1 || n_q > S) return 0;
     return layer_ws_bytes(*g, n_q);
+  }
+  if (op == SVG_OP_KMEANS) {
+    const int32_t S = g->F * g->HH * g->WW;
+    if (n_q < 1 || n_q > S || n_q > KMEANS_MAX_C) return 0;
+    return kmeans_ws(*g, n_q).total;
+  }
+  if (op == SVG_OP_CLUSTER_ATTN) {
+    const int32_t S = g->F * g->HH * g->WW;
+    if (n_q < 1 || n_q > S || n_q > CLUSTER_MAX_CQ) return 0;
+    return cluster_ws(*g, n_q).total;
   }
   return 0;
 }

@@ -321,63 +321,94 @@ struct RowMap {
   }
 };
 
+// Where a workgroup's rows and keys come from.  Rows are numbered in a logical order (the
+// head's working layout, or a query cluster's sorted rows); each source maps a logical query
+// or key to the row of the tensor that holds it, clamping past the end (such rows are masked or
+// not stored; q_row_in takes rows below the row count), and gives each query's allowed keys
+// (u below the row count) as one interval of logical key positions.
+//
+// BandSource: a head of the spatial/temporal path; keys are the same rows as queries and each
+// query's interval follows from its band.
+struct BandSource {
+  static constexpr bool kGather = false;
+  RowMap rmap;
+  Band band;
+  int32_t S;
+  __device__ __forceinline__ int32_t q_row(int32_t u) const { return rmap(min(u, S - 1)); }
+  __device__ __forceinline__ int32_t q_row_in(int32_t u) const { return rmap(u); }
+  __device__ __forceinline__ int32_t kv_row(int32_t j) const { return rmap(min(j, S - 1)); }
+  __device__ __forceinline__ void interval(int32_t u, int32_t& lo, int32_t& hi) const {
+    band_interval(band, u, lo, hi);
+  }
+};
+// ClusterSource: the rows of one query cluster (sorted positions -> tokens) against the key
+// list of that cluster (the concatenated tokens of its selected key clusters), all of which
+// every query attends to.  Key rows are read from the list, one phase ahead.
+struct ClusterSource {
+  static constexpr bool kGather = true;
+  const int32_t* qp;           // tokens of the query cluster
+  const int32_t* kl;           // its key list
+  int32_t n, L;
+  int32_t S;
+  __device__ __forceinline__ int32_t q_row(int32_t u) const { return min(max(qp[min(u, n - 1)], 0), S - 1); }
+  __device__ __forceinline__ int32_t q_row_in(int32_t u) const { return min(max(qp[u], 0), S - 1); }
+  __device__ __forceinline__ int32_t kv_row(int32_t j) const { return kl[min(j, L - 1)]; }
+  __device__ __forceinline__ void interval(int32_t, int32_t& lo, int32_t& hi) const {
+    lo = 0;
+    hi = L;
+  }
+};
+
 // Copy of one K or V tile into LDS by the four wavefronts of one group (wb = 0..3): per
 // wavefront, PER_WAVE instructions of 1 KB each.  The address is the wavefront-uniform head
-// base plus a 32-bit per-lane offset (the host checks that a head fits in 4 GB); rows past
-// the sequence end repeat its last row.  Every lane copies 16 bytes of one row, so the rows
-// of a tile may come from anywhere: the row map gathers them.
+// base plus a 32-bit per-lane offset (the host checks that a head fits in 4 GB).  Every lane
+// copies 16 bytes of one row, so the rows of a tile may come from anywhere: row_of(i, r) is the
+// tensor row that instruction i of this lane reads for tile row r.
 template <int D>
-__device__ __forceinline__ void pp_load(const bf16* __restrict__ src, int32_t k0, int32_t S, bf16* dst, int wb,
-                                        int lane, bool is_v, const RowMap& rmap) {
+struct CopyPlan {
+  static constexpr int PER_WAVE = TileLds<D>::TILE_BYTES / 1024 / 4;
+  static constexpr int RPI = 1024 / TileLds<D>::ROW_BYTES;    // tile rows per instruction
+};
+
+template <int D, class RowOf>
+__device__ __forceinline__ void pp_load(const bf16* __restrict__ src, bf16* dst, int wb, int lane, bool is_v,
+                                        RowOf row_of) {
   using T = TileLds<D>;
-  constexpr int PER_WAVE = T::TILE_BYTES / 1024 / 4;
-  constexpr int RPI = 1024 / T::ROW_BYTES;                // tile rows per instruction
+  using CP = CopyPlan<D>;
   const int pc = lane % T::CPR;
 #pragma unroll
-  for (int i = 0; i < PER_WAVE; ++i) {
-    const int kb = (wb * PER_WAVE + i) * 1024;
-    const int row = (wb * PER_WAVE + i) * RPI + lane / T::CPR;
+  for (int i = 0; i < CP::PER_WAVE; ++i) {
+    const int kb = (wb * CP::PER_WAVE + i) * 1024;
+    const int row = (wb * CP::PER_WAVE + i) * CP::RPI + lane / T::CPR;
     const int lc = pc ^ (is_v ? T::swz_v(row) : T::swz_k(row));
-    const uint32_t boff = (uint32_t)rmap(min(k0 + row, S - 1)) * (uint32_t)T::ROW_BYTES + 16u * (uint32_t)lc;
+    const uint32_t boff = (uint32_t)row_of(i, row) * (uint32_t)T::ROW_BYTES + 16u * (uint32_t)lc;
     __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(src) + boff,
                                      (__attribute__((address_space(3))) void*)((char*)dst + kb), 16, 0, 0);
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(PP_NT, 1) void attn_fwd_kernel(AttnArgs a, int32_t nqb) {
+// Tensor rows of the tile at logical key k0 that this lane copies, read ahead of the copy.
+template <int D, class Src>
+__device__ __forceinline__ void tile_rows(const Src& src, int32_t k0, int wb, int lane,
+                                          int32_t (&prow)[CopyPlan<D>::PER_WAVE]) {
+  using CP = CopyPlan<D>;
+#pragma unroll
+  for (int i = 0; i < CP::PER_WAVE; ++i)
+    prow[i] = src.kv_row(k0 + (wb * CP::PER_WAVE + i) * CP::RPI + lane / TileLds<D>::CPR);
+}
+
+// The ping-pong loop of one workgroup: 256 logical query rows from q0 (rows at or past n_rows
+// are computed on clamped inputs and not stored).
+template <int D, class Src>
+__device__ __forceinline__ void pp_attention(const Src& src, const bf16* __restrict__ Q, const bf16* __restrict__ K,
+                                             const bf16* __restrict__ V, bf16* __restrict__ O, int32_t n_rows,
+                                             int32_t q0, float scale) {
   constexpr int NDB = D / 32;
   constexpr int NKS = D / 16;
+  constexpr int PW = CopyPlan<D>::PER_WAVE;
   __shared__ __attribute__((aligned(1024))) bf16 K0[BN * D];
   __shared__ __attribute__((aligned(1024))) bf16 K1[BN * D];
   __shared__ __attribute__((aligned(1024))) bf16 Vb[3][BN * D];     // V(t_j) in Vb[j % 3]
-
-  const int32_t item = xcd_item((int32_t)blockIdx.x, (int32_t)gridDim.x);
-  const int32_t rank = item / nqb;
-  const int32_t qb = item - rank * nqb;
-  const int32_t bh = a.order ? a.order[rank] : rank;
-  int kind = (a.force_dense || a.kind == nullptr) ? KIND_DENSE : (int)a.kind[bh];
-  if (kind != KIND_SPATIAL && kind != KIND_TEMPORAL) kind = KIND_DENSE;
-  const bool tmaj = kind == KIND_TEMPORAL;
-  // temporal heads work in token-major order; they read token-major copies (qt, kt, vt -> ot)
-  // or, fused, the frame-major tensors through the row map
-  const bool own_t = tmaj && !a.fused_t;
-  const size_t off = (size_t)bh * (size_t)a.S * D;
-  const bf16* __restrict__ Q = (own_t ? a.qt : a.q) + off;
-  const bf16* __restrict__ K = (own_t ? a.kt : a.k) + off;
-  const bf16* __restrict__ V = (own_t ? a.vt : a.v) + off;
-  bf16* __restrict__ O = (own_t ? a.ot : a.o) + off;
-  RowMap rmap;
-  rmap.divF = a.divF;
-  rmap.F = a.F;
-  rmap.P = a.P;
-  rmap.tm = tmaj && a.fused_t;
-
-  Band band;
-  band.S = a.S;
-  band.dense = kind == KIND_DENSE;
-  if (tmaj) { band.divG = a.divF; band.G = a.F; band.NG = a.P; band.w = a.w_p; }
-  else { band.divG = a.divP; band.G = a.P; band.NG = a.F; band.w = a.w_f; }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -389,36 +420,43 @@ __global__ __launch_bounds__(PP_NT, 1) void attn_fwd_kernel(AttnArgs a, int32_t 
   const int hh = lane >> 5;
 
   // tiles of the whole workgroup (union of both groups' ranges)
-  const int32_t q0 = qb * PP_BM;
-  const int32_t q_last = min(q0 + PP_BM, a.S) - 1;
+  const int32_t q_last = min(q0 + PP_BM, n_rows) - 1;
   int32_t lo0, hi0, lo1, hi1;
-  band_interval(band, q0, lo0, hi0);
-  band_interval(band, q_last, lo1, hi1);
+  src.interval(q0, lo0, hi0);
+  src.interval(q_last, lo1, hi1);
   const int32_t t_begin = lo0 / BN;
   const int32_t T = (hi1 + BN - 1) / BN - t_begin;
 
   // this group's rows and tiles
   const int32_t g0 = q0 + grp * (PP_BM / 2);
-  const bool g_live = g0 < a.S;
-  const int32_t g1 = min(g0 + PP_BM / 2, a.S) - 1;
+  const bool g_live = g0 < n_rows;
+  const int32_t g1 = min(g0 + PP_BM / 2, n_rows) - 1;
   int32_t glo_first = 0, ghi_first = 0, glo_last = 0, ghi_last = 0;
   if (g_live) {
-    band_interval(band, g0, glo_first, ghi_first);
-    band_interval(band, g1, glo_last, ghi_last);
+    src.interval(g0, glo_first, ghi_first);
+    src.interval(g1, glo_last, ghi_last);
   }
 
   const int32_t my_q = g0 + wig * 32 + l32;
-  const int32_t my_qc = min(my_q, a.S - 1);
   int32_t my_lo, my_hi;
-  band_interval(band, my_qc, my_lo, my_hi);
+  src.interval(min(my_q, n_rows - 1), my_lo, my_hi);
 
   // first tiles: K(t_0) by group A, V(t_0) by group B
-  if (grp == 0) pp_load<D>(K, t_begin * BN, a.S, K0, wig, lane, false, rmap);
-  else pp_load<D>(V, t_begin * BN, a.S, Vb[0], wig, lane, true, rmap);
+  {
+    const int32_t k0 = t_begin * BN;
+    auto rows = [&](int, int r) { return src.kv_row(k0 + r); };
+    if (grp == 0) pp_load<D>(K, K0, wig, lane, false, rows);
+    else pp_load<D>(V, Vb[0], wig, lane, true, rows);
+  }
+  // gathered key rows of the copy that follows this group's next matrix phase
+  int32_t nrow[PW];
+  if constexpr (Src::kGather) tile_rows<D>(src, (t_begin + 1) * BN, wig, lane, nrow);
   bf16x8 qf[NKS];
+  {
+    const bf16* qrow = Q + (size_t)src.q_row(my_q) * D;
 #pragma unroll
-  for (int s = 0; s < NKS; ++s)
-    qf[s] = *reinterpret_cast<const bf16x8*>(Q + (size_t)rmap(my_qc) * D + 16 * s + 8 * hh);
+    for (int s = 0; s < NKS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * hh);
+  }
 
   RowState<D> st;
 #pragma unroll
@@ -431,7 +469,7 @@ __global__ __launch_bounds__(PP_NT, 1) void attn_fwd_kernel(AttnArgs a, int32_t 
   st.l_run = 0.f;
   // M(0) reads V(t_{-1}) from Vb[2] with P^T = 0: zero it so that the product is exactly zero
   for (int o = tid; o < BN * D / 8; o += PP_NT) reinterpret_cast<u32x4*>(Vb[2])[o] = u32x4{0u, 0u, 0u, 0u};
-  const float c = a.scale * 1.44269504088896340736f;
+  const float c = scale * 1.44269504088896340736f;
   const int tg = lane >> 4;
   const int ti = lane & 15;
   const int v_row = 4 * (tg >> 1) + (ti >> 2);
@@ -457,7 +495,8 @@ __global__ __launch_bounds__(PP_NT, 1) void attn_fwd_kernel(AttnArgs a, int32_t 
     phase_m<D>(st, qf, reinterpret_cast<const char*>(vprev), reinterpret_cast<const char*>(kcur), v_row, v_col, l32,
                hh, av0);
   };
-  // after a group's vector phase and its copies: the first V^T operand of its next matrix phase
+  // after a group's vector phase X(i) and its copies: the first V^T operand of its next matrix
+  // phase, and (gathered keys) the rows of the copy that follows that phase, tile i + 2
   auto pre = [&](const bf16* vnext) {
 #pragma unroll
     for (int j = 0; j < NPRE; ++j) av0[j] = read_vt0<D>(reinterpret_cast<const char*>(vnext), v_row, v_col, j);
@@ -465,14 +504,26 @@ __global__ __launch_bounds__(PP_NT, 1) void attn_fwd_kernel(AttnArgs a, int32_t 
   auto do_x = [&](int32_t i) {
     __builtin_amdgcn_s_setprio(0);
     phase_softmax<D>(st, (t_begin + i) * BN, edge(i), my_lo, my_hi, c, hh);
+    if constexpr (Src::kGather) tile_rows<D>(src, (t_begin + i + 2) * BN, wig, lane, nrow);
     __builtin_amdgcn_s_setprio(2);
   };
   // copies after M(j): group A K(t_{j+1}) -> kdst, group B V(t_{j+1}) -> Vb[(j+1) % 3]
+  auto rows_of = [&](int32_t j) {
+    const int32_t k0 = (t_begin + j + 1) * BN;
+    return [&, k0](int i, int r) {
+      if constexpr (Src::kGather) {
+        (void)k0;
+        return nrow[i];
+      } else {
+        return src.kv_row(k0 + r);
+      }
+    };
+  };
   auto copy_k = [&](int32_t j, bf16* kdst) {
-    if (j + 1 < T) pp_load<D>(K, (t_begin + j + 1) * BN, a.S, kdst, wig, lane, false, rmap);
+    if (j + 1 < T) pp_load<D>(K, kdst, wig, lane, false, rows_of(j));
   };
   auto copy_v = [&](int32_t j) {
-    if (j + 1 < T) pp_load<D>(V, (t_begin + j + 1) * BN, a.S, Vb[(j + 1) % 3], wig, lane, true, rmap);
+    if (j + 1 < T) pp_load<D>(V, Vb[(j + 1) % 3], wig, lane, true, rows_of(j));
   };
   auto vbuf = [&](int32_t j) { return Vb[(j + 3) % 3]; };   // V(t_j), j >= -1
 
@@ -525,10 +576,10 @@ __global__ __launch_bounds__(PP_NT, 1) void attn_fwd_kernel(AttnArgs a, int32_t 
   }
 
   // ---- epilogue: divide by the row sum, round to bf16, store this lane's query row ----
-  if (my_q < a.S) {
+  if (my_q < n_rows) {
     const float l_tot = st.l_run + other_half(st.l_run);
     const float inv = 1.f / l_tot;
-    bf16* orow = O + (size_t)rmap(my_q) * D;
+    bf16* orow = O + (size_t)src.q_row_in(my_q) * D;
 #pragma unroll
     for (int j = 0; j < NDB; ++j)
 #pragma unroll
@@ -540,6 +591,63 @@ __global__ __launch_bounds__(PP_NT, 1) void attn_fwd_kernel(AttnArgs a, int32_t 
       }
   }
 }
+
+template <int D>
+__global__ __launch_bounds__(PP_NT, 1) void attn_fwd_kernel(AttnArgs a, int32_t nqb) {
+  const int32_t item = xcd_item((int32_t)blockIdx.x, (int32_t)gridDim.x);
+  const int32_t rank = item / nqb;
+  const int32_t qb = item - rank * nqb;
+  const int32_t bh = a.order ? a.order[rank] : rank;
+  int kind = (a.force_dense || a.kind == nullptr) ? KIND_DENSE : (int)a.kind[bh];
+  if (kind != KIND_SPATIAL && kind != KIND_TEMPORAL) kind = KIND_DENSE;
+  const bool tmaj = kind == KIND_TEMPORAL;
+  // temporal heads work in token-major order; they read token-major copies (qt, kt, vt -> ot)
+  // or, fused, the frame-major tensors through the row map
+  const bool own_t = tmaj && !a.fused_t;
+  const size_t off = (size_t)bh * (size_t)a.S * D;
+  BandSource src;
+  src.rmap.divF = a.divF;
+  src.rmap.F = a.F;
+  src.rmap.P = a.P;
+  src.rmap.tm = tmaj && a.fused_t;
+  src.S = a.S;
+  src.band.S = a.S;
+  src.band.dense = kind == KIND_DENSE;
+  if (tmaj) { src.band.divG = a.divF; src.band.G = a.F; src.band.NG = a.P; src.band.w = a.w_p; }
+  else { src.band.divG = a.divP; src.band.G = a.P; src.band.NG = a.F; src.band.w = a.w_f; }
+  pp_attention<D>(src, (own_t ? a.qt : a.q) + off, (own_t ? a.kt : a.k) + off, (own_t ? a.vt : a.v) + off,
+                  (own_t ? a.ot : a.o) + off, a.S, qb * PP_BM, a.scale);
+}
+
+// One workgroup per (head, query cluster, 256-row tile of that cluster); unused item slots of a
+// head (-1) exit at once.
+template <int D>
+__global__ __launch_bounds__(PP_NT, 1) void cluster_attn_kernel(ClusterAttnArgs a) {
+  const int32_t item = xcd_item((int32_t)blockIdx.x, (int32_t)gridDim.x);
+  const int32_t bh = item / a.items_per_head;
+  const int32_t code = a.items[item];
+  if (code < 0) return;
+  const int32_t qc = code >> 16, qt = code & 0xFFFF;
+  const int32_t* qoff = a.q_off + (size_t)bh * (a.Cq + 1);
+  // (offsets and list lengths are clamped into range: inconsistent inputs cannot address
+  // memory outside the buffers; the key lists hold in-range rows)
+  const int32_t qbeg = min(max(qoff[qc], 0), a.S);
+  ClusterSource src;
+  src.S = a.S;
+  src.n = min(max(qoff[qc + 1] - qbeg, 0), a.S - qbeg);
+  src.L = min(max(a.klen[(size_t)bh * a.Cq + qc], 0), a.S);
+  if (src.n == 0 || src.L == 0) return;
+  src.qp = a.q_perm + (size_t)bh * a.S + qbeg;
+  src.kl = a.klist + ((size_t)bh * a.Cq + qc) * a.S;
+  const size_t off = (size_t)bh * (size_t)a.S * D;
+  pp_attention<D>(src, a.q + off, a.k + off, a.v + off, a.o + off, src.n, qt * PP_BM, a.scale);
+}
+
+// Explicit instantiations, so that the host pass emits every launch stub the launchers use.
+template __global__ void attn_fwd_kernel<128>(AttnArgs, int32_t);
+template __global__ void attn_fwd_kernel<64>(AttnArgs, int32_t);
+template __global__ void cluster_attn_kernel<128>(ClusterAttnArgs);
+template __global__ void cluster_attn_kernel<64>(ClusterAttnArgs);
 
 }  // namespace
 
@@ -557,6 +665,19 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
     attn_fwd_kernel<128><<<grid, PP_NT, 0, st>>>(b, nqb);
   } else if (a.D == 64) {
     attn_fwd_kernel<64><<<grid, PP_NT, 0, st>>>(b, nqb);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_cluster_attention(const ClusterAttnArgs& a, hipStream_t st) {
+  static_assert(CLUSTER_TILE_ROWS == PP_BM, "cluster work items are attention workgroups");
+  const dim3 grid((unsigned)((int64_t)a.items_per_head * a.BH));
+  if (a.D == 128) {
+    cluster_attn_kernel<128><<<grid, PP_NT, 0, st>>>(a);
+  } else if (a.D == 64) {
+    cluster_attn_kernel<64><<<grid, PP_NT, 0, st>>>(a);
   } else {
     return hipErrorInvalidValue;
   }

@@ -1,0 +1,504 @@
+// Semantic clustering path (Sparse VideoGen2, technical summary of the explainer page, section 2):
+// k-means of the Q and K rows of every head, the permutation that makes each cluster contiguous,
+// centroid-based top-p selection of key clusters per query cluster, and the key lists the
+// attention kernel gathers from.
+//
+// k-means (section 2A) is Lloyd's iteration: every row goes to the nearest centroid, then every
+// centroid moves to the mean of its rows.  The assignment is a dense contraction (rows x
+// centroids over D) and runs on the matrix cores: centroids are rounded to bf16, the bf16 rows
+// are multiplied against them with fp32 accumulation, and each row keeps the centroid with the
+// largest x.c - |c|^2 / 2 (the smallest distance; ties to the lowest index).  The update first
+// sorts the tokens by cluster with a stable counting sort (the permutation of section 2A) and
+// then averages each cluster's rows in fp64, so the centroids do not depend on the order in
+// which the hardware happens to run.
+//
+// The top-p selection (section 2B) is tiny (C_q x C_k centroid products per head) and runs in
+// fp64: the estimated share of attention of key cluster j for query cluster i is
+// n_j exp(s_ij) / sum_j' n_j' exp(s_ij'), s_ij = scale * c_qi . c_kj (a centroid stands for all
+// n_j keys of its cluster); key clusters are taken in decreasing share until the shares reach p.
+#include "svg_internal.h"
+
+namespace svg {
+
+namespace {
+
+constexpr int AS_BM = 128;     // rows per assignment workgroup (4 wavefronts x 32)
+constexpr int AS_BN = 64;      // centroids per LDS tile
+constexpr int AS_NT = 256;
+
+// Rounds every centroid to bf16 and stores half its squared norm (of the rounded values);
+// padding centroids past C get +inf, so that they never win.
+__global__ void kmeans_prep_kernel(const float* __restrict__ cent, bf16* __restrict__ cb, float* __restrict__ hn,
+                                   int32_t BH, int32_t C, int32_t Cpad, int32_t D) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)BH * Cpad) return;
+  const int32_t bh = (int32_t)(i / Cpad), c = (int32_t)(i - (int64_t)bh * Cpad);
+  bf16* dst = cb + i * D;
+  if (c >= C) {
+    for (int d = 0; d < D; ++d) dst[d] = (bf16)0.f;
+    hn[i] = INFINITY;
+    return;
+  }
+  const float* src = cent + ((int64_t)bh * C + c) * D;
+  float s = 0.f;
+  for (int d = 0; d < D; ++d) {
+    const bf16 b = (bf16)src[d];
+    dst[d] = b;
+    const float f = (float)b;
+    s = fmaf(f, f, s);
+  }
+  hn[i] = 0.5f * s;
+}
+
+// Cold start: centroid c of every head is the row at token idx[c] (clamped into [0, S)).
+__global__ void kmeans_init_kernel(const bf16* __restrict__ x, const int32_t* __restrict__ idx, float* __restrict__ cent,
+                                   int32_t BH, int32_t S, int32_t C, int32_t D) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)BH * C * D) return;
+  const int32_t d = (int32_t)(i % D);
+  const int64_t r = i / D;
+  const int32_t c = (int32_t)(r % C);
+  const int32_t bh = (int32_t)(r / C);
+  const int32_t t = min(max(idx[c], 0), S - 1);
+  cent[i] = (float)x[((int64_t)bh * S + t) * D + d];
+}
+
+// Nearest centroid of 128 rows per workgroup.  Wavefront w holds rows 32w..32w+31 as the B
+// operand of v_mfma_f32_32x32x16_bf16 (one row per lane column); tiles of 64 centroids are the
+// A operand from LDS.  The accumulator gives each lane one row and 16 centroids per 32-block, in
+// increasing centroid order, so a strict comparison keeps the lowest index among equals.
+template <int D>
+__global__ __launch_bounds__(AS_NT) void kmeans_assign_kernel(const bf16* __restrict__ x, const bf16* __restrict__ cb,
+                                                              const float* __restrict__ hn, int32_t* __restrict__ labels,
+                                                              int32_t S, int32_t Cpad, int32_t nrb) {
+  constexpr int NKS = D / 16;
+  constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  constexpr int RPB = 16 / CPR;               // rows per 256-byte bank period
+  __shared__ __attribute__((aligned(16))) bf16 ct[AS_BN * D];
+  __shared__ float th[AS_BN];
+
+  const int32_t bh = blockIdx.x / nrb;
+  const int32_t rb = blockIdx.x - bh * nrb;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int32_t row = rb * AS_BM + wave * 32 + l32;
+  const bf16* xh = x + (size_t)bh * S * D;
+  const bf16* cbh = cb + (size_t)bh * Cpad * D;
+  const float* hnh = hn + (size_t)bh * Cpad;
+
+  bf16x8 xf[NKS];
+  const bf16* xr = xh + (size_t)min(row, S - 1) * D;
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) xf[s] = *reinterpret_cast<const bf16x8*>(xr + 16 * s + 8 * hh);
+
+  float best = -INFINITY;
+  int32_t best_c = 0;
+  for (int32_t c0 = 0; c0 < Cpad; c0 += AS_BN) {
+    __syncthreads();
+    // 16-byte chunk q of tile row r goes to slot q ^ ((r / RPB) & (CPR - 1)) of the row
+    for (int o = tid; o < AS_BN * CPR; o += AS_NT) {
+      const int r = o / CPR, q = o % CPR;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(cbh + (size_t)(c0 + r) * D + 8 * q);
+      *reinterpret_cast<u32x4*>(ct + r * D + 8 * (q ^ ((r / RPB) & (CPR - 1)))) = v;
+    }
+    if (tid < AS_BN) th[tid] = hnh[c0 + tid];
+    __syncthreads();
+    f32x16 acc[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[blk][r] = 0.f;
+#pragma unroll
+    for (int s = 0; s < NKS; ++s)
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        const int r = blk * 32 + l32;
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ct + r * D + 8 * ((2 * s + hh) ^ ((r / RPB) & (CPR - 1))));
+        acc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, xf[s], acc[blk], 0, 0, 0);
+      }
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int cl = blk * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+        const float sc = acc[blk][r] - th[cl];
+        if (sc > best) {
+          best = sc;
+          best_c = c0 + cl;
+        }
+      }
+  }
+  // the two lane halves hold interleaved centroids: larger score wins, then lower index
+  const auto rb2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(best), __float_as_uint(best), false, false);
+  const auto rc2 = __builtin_amdgcn_permlane32_swap((uint32_t)best_c, (uint32_t)best_c, false, false);
+  const float ob = __uint_as_float(hh ? rb2[0] : rb2[1]);
+  const int32_t oc = (int32_t)(hh ? rc2[0] : rc2[1]);
+  if (ob > best || (ob == best && oc < best_c)) best_c = oc;
+  if (hh == 0 && row < S) labels[(size_t)bh * S + row] = best_c;
+}
+
+constexpr int CHUNK = 1024;     // tokens per counting-sort chunk
+
+// counts[bh][chunk][c]: tokens of the chunk in cluster c.
+__global__ void cluster_hist_kernel(const int32_t* __restrict__ labels, int32_t* __restrict__ counts, int32_t S,
+                                    int32_t C, int32_t nchunk) {
+  extern __shared__ int32_t cnt[];
+  const int32_t chunk = blockIdx.x, bh = blockIdx.y;
+  for (int c = threadIdx.x; c < C; c += blockDim.x) cnt[c] = 0;
+  __syncthreads();
+  const int32_t t0 = chunk * CHUNK, t1 = min(t0 + CHUNK, S);
+  for (int32_t t = t0 + threadIdx.x; t < t1; t += blockDim.x)
+    atomicAdd(&cnt[min(max(labels[(size_t)bh * S + t], 0), C - 1)], 1);
+  __syncthreads();
+  int32_t* out = counts + ((size_t)bh * nchunk + chunk) * C;
+  for (int c = threadIdx.x; c < C; c += blockDim.x) out[c] = cnt[c];
+}
+
+// In place: counts[bh][chunk][c] -> first sorted position of chunk's tokens of cluster c
+// (clusters in index order, chunks in order inside a cluster); offsets[bh][c] = start of
+// cluster c, offsets[bh][C] = S.
+constexpr int SCAN_NT = 1024;
+__global__ __launch_bounds__(SCAN_NT) void cluster_scan_kernel(int32_t* __restrict__ counts,
+                                                               int32_t* __restrict__ offsets, int32_t S, int32_t C,
+                                                               int32_t nchunk) {
+  __shared__ int32_t part[SCAN_NT];
+  const int32_t bh = blockIdx.x;
+  const int tid = threadIdx.x;
+  int32_t* cnt = counts + (size_t)bh * nchunk * C;
+  // thread tid owns clusters [tid * per, (tid + 1) * per)
+  const int per = (C + SCAN_NT - 1) / SCAN_NT;
+  const int c_lo = min(tid * per, C), c_hi = min(c_lo + per, C);
+  int32_t own = 0;
+  for (int c = c_lo; c < c_hi; ++c)
+    for (int32_t k = 0; k < nchunk; ++k) own += cnt[(size_t)k * C + c];
+  part[tid] = own;
+  __syncthreads();
+  // inclusive scan of the per-thread totals (Hillis-Steele)
+  for (int o = 1; o < SCAN_NT; o <<= 1) {
+    const int32_t v = tid >= o ? part[tid - o] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int32_t run = part[tid] - own;
+  int32_t* off = offsets + (size_t)bh * (C + 1);
+  for (int c = c_lo; c < c_hi; ++c) {
+    off[c] = run;
+    for (int32_t k = 0; k < nchunk; ++k) {
+      const int32_t n = cnt[(size_t)k * C + c];
+      cnt[(size_t)k * C + c] = run;
+      run += n;
+    }
+  }
+  if (tid == 0) off[C] = S;
+}
+
+// Stable scatter: one wavefront walks its chunk 64 tokens at a time; tokens of one round with
+// equal labels are ranked by lane, and rounds go in token order.  (Labels and the indices read
+// from them are clamped in range here and below, so that inconsistent inputs cannot address
+// memory outside the buffers.)
+__global__ __launch_bounds__(64) void cluster_scatter_kernel(const int32_t* __restrict__ labels,
+                                                             const int32_t* __restrict__ base,
+                                                             int32_t* __restrict__ perm, int32_t S, int32_t C,
+                                                             int32_t nchunk) {
+  extern __shared__ int32_t ctr[];
+  const int32_t chunk = blockIdx.x, bh = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int32_t* b = base + ((size_t)bh * nchunk + chunk) * C;
+  for (int c = lane; c < C; c += 64) ctr[c] = b[c];
+  __syncthreads();
+  const int32_t t0 = chunk * CHUNK, t1 = min(t0 + CHUNK, S);
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int32_t r0 = t0; r0 < t1; r0 += 64) {
+    const int32_t t = r0 + lane;
+    const bool valid = t < t1;
+    const int32_t lab = valid ? min(max(labels[(size_t)bh * S + t], 0), C - 1) : -1;
+    uint64_t pending = __ballot(valid);
+    int32_t pos = 0;
+    while (pending) {
+      const int leader = __builtin_ctzll(pending);
+      const int32_t L = __shfl(lab, leader);
+      const uint64_t same = __ballot(lab == L) & pending;
+      if (lab == L) pos = ctr[L] + __popcll(same & below);
+      __builtin_amdgcn_wave_barrier();
+      if (lane == leader) ctr[L] += __popcll(same);
+      __builtin_amdgcn_wave_barrier();
+      pending &= ~same;
+    }
+    if (valid) perm[(size_t)bh * S + pos] = t;
+  }
+}
+
+// Mean of each cluster's rows in fp64 (rows in sorted order, four wavefronts interleaved, a
+// fixed reduction order); an empty cluster keeps its centroid.
+template <int D>
+__global__ __launch_bounds__(256) void kmeans_update_kernel(const bf16* __restrict__ x, const int32_t* __restrict__ perm,
+                                                            const int32_t* __restrict__ offsets,
+                                                            float* __restrict__ cent, int32_t S, int32_t C) {
+  constexpr int CPL = D / 64;    // columns per lane
+  __shared__ double red[4][D];
+  const int32_t c = blockIdx.x, bh = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int32_t* off = offsets + (size_t)bh * (C + 1);
+  const int32_t j0 = off[c], j1 = off[c + 1];
+  if (j1 == j0) return;
+  const bf16* xh = x + (size_t)bh * S * D;
+  const int32_t* ph = perm + (size_t)bh * S;
+  double acc[CPL];
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) acc[e] = 0.0;
+  for (int32_t j = j0 + wave; j < j1; j += 4) {
+    const bf16* r = xh + (size_t)min(max(ph[j], 0), S - 1) * D + CPL * lane;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) acc[e] += (double)(float)r[e];
+  }
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) red[wave][CPL * lane + e] = acc[e];
+  __syncthreads();
+  if (tid < D) {
+    const double s = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+    cent[((size_t)bh * C + c) * D + tid] = (float)(s / (double)(j1 - j0));
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Centroid top-p selection, one workgroup per (head, query cluster).
+// ---------------------------------------------------------------------------------------------
+constexpr int TP_NT = 256;
+constexpr int TP_MAXC = 1024;
+
+__global__ __launch_bounds__(TP_NT) void centroid_topp_kernel(const float* __restrict__ cq, const float* __restrict__ ck,
+                                                              const int32_t* __restrict__ k_off,
+                                                              uint8_t* __restrict__ sel, int32_t Cq, int32_t Ck,
+                                                              int32_t D, double scale, double p) {
+  __shared__ double qv[128];
+  __shared__ double w[TP_MAXC];
+  __shared__ int32_t ix[TP_MAXC];
+  __shared__ double red[TP_NT];
+  const int32_t i = blockIdx.x, bh = blockIdx.y;
+  const int tid = threadIdx.x;
+  const float* qrow = cq + ((size_t)bh * Cq + i) * D;
+  const float* kh = ck + (size_t)bh * Ck * D;
+  const int32_t* off = k_off + (size_t)bh * (Ck + 1);
+  for (int d = tid; d < D; d += TP_NT) qv[d] = (double)qrow[d];
+  __syncthreads();
+  // scores; empty key clusters get -inf
+  double mx = -INFINITY;
+  for (int j = tid; j < Ck; j += TP_NT) {
+    const float* kr = kh + (size_t)j * D;
+    double s = 0.0;
+    for (int d = 0; d < D; ++d) s = fma(qv[d], (double)kr[d], s);
+    s = (off[j + 1] > off[j]) ? scale * s : -INFINITY;
+    w[j] = s;
+    mx = fmax(mx, s);
+  }
+  red[tid] = mx;
+  __syncthreads();
+  for (int o = TP_NT / 2; o > 0; o >>= 1) {
+    if (tid < o) red[tid] = fmax(red[tid], red[tid + o]);
+    __syncthreads();
+  }
+  mx = red[0];
+  __syncthreads();
+  double z = 0.0;
+  for (int j = tid; j < Ck; j += TP_NT) {
+    const double e = (double)(off[j + 1] - off[j]) * exp(w[j] - mx);
+    w[j] = e;
+    z += e;
+  }
+  red[tid] = z;
+  __syncthreads();
+  for (int o = TP_NT / 2; o > 0; o >>= 1) {
+    if (tid < o) red[tid] += red[tid + o];
+    __syncthreads();
+  }
+  z = red[0];
+  // shares, padded to a power of two with entries that sort last
+  int n2 = 1;
+  while (n2 < Ck) n2 <<= 1;
+  for (int j = tid; j < n2; j += TP_NT) {
+    if (j < Ck) {
+      w[j] = w[j] / z;
+      ix[j] = j;
+    } else {
+      w[j] = -1.0;
+      ix[j] = j;
+    }
+  }
+  __syncthreads();
+  // bitonic sort: decreasing share, increasing index among equal shares
+  for (int k = 2; k <= n2; k <<= 1)
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      for (int a = tid; a < n2; a += TP_NT) {
+        const int b = a ^ jj;
+        if (b > a) {
+          const bool up = (a & k) == 0;
+          const double wa = w[a], wb = w[b];
+          const int32_t ia = ix[a], ib = ix[b];
+          const bool a_first = wa > wb || (wa == wb && ia < ib);
+          if (a_first != up) {
+            w[a] = wb; w[b] = wa;
+            ix[a] = ib; ix[b] = ia;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  uint8_t* srow = sel + ((size_t)bh * Cq + i) * Ck;
+  for (int j = tid; j < Ck; j += TP_NT) srow[j] = 0;
+  __syncthreads();
+  // the shortest prefix reaching p, summed in order
+  if (tid == 0) {
+    double acc = 0.0;
+    for (int r = 0; r < Ck; ++r) {
+      if (w[r] <= 0.0) break;
+      srow[ix[r]] = 1;
+      acc += w[r];
+      if (acc >= p) break;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Key list of each (head, query cluster): the sorted positions of its selected key clusters, in
+// cluster order, mapped to token rows; and its length.
+// ---------------------------------------------------------------------------------------------
+constexpr int KL_NT = 256;
+__global__ __launch_bounds__(KL_NT) void cluster_keylist_kernel(const uint8_t* __restrict__ sel,
+                                                                const int32_t* __restrict__ k_perm,
+                                                                const int32_t* __restrict__ k_off,
+                                                                int32_t* __restrict__ klist, int32_t* __restrict__ klen,
+                                                                int32_t S, int32_t Cq, int32_t Ck) {
+  __shared__ int32_t start[TP_MAXC + 1];   // first list position of the m-th selected cluster
+  __shared__ int32_t cid[TP_MAXC];         // its cluster index
+  __shared__ int32_t part[KL_NT];
+  const int32_t i = blockIdx.x, bh = blockIdx.y;
+  const int tid = threadIdx.x;
+  const uint8_t* srow = sel + ((size_t)bh * Cq + i) * Ck;
+  const int32_t* off = k_off + (size_t)bh * (Ck + 1);
+  // thread tid owns clusters [tid * per, ...): selected count and key count
+  const int per = (Ck + KL_NT - 1) / KL_NT;
+  const int c_lo = min(tid * per, Ck), c_hi = min(c_lo + per, Ck);
+  int32_t nsel = 0, nkey = 0;
+  for (int c = c_lo; c < c_hi; ++c)
+    if (srow[c]) { ++nsel; nkey += off[c + 1] - off[c]; }
+  // scan of (nsel, nkey) packed: nkey < 2^31 / ... kept separate for clarity
+  part[tid] = nsel;
+  __syncthreads();
+  for (int o = 1; o < KL_NT; o <<= 1) {
+    const int32_t v = tid >= o ? part[tid - o] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int32_t m = part[tid] - nsel;
+  const int32_t msel = part[KL_NT - 1];
+  __syncthreads();
+  part[tid] = nkey;
+  __syncthreads();
+  for (int o = 1; o < KL_NT; o <<= 1) {
+    const int32_t v = tid >= o ? part[tid - o] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int32_t pos = part[tid] - nkey;
+  const int32_t L = part[KL_NT - 1];
+  for (int c = c_lo; c < c_hi; ++c)
+    if (srow[c]) {
+      start[m] = pos;
+      cid[m] = c;
+      ++m;
+      pos += off[c + 1] - off[c];
+    }
+  if (tid == 0) {
+    start[msel] = L;
+    klen[(size_t)bh * Cq + i] = L;
+  }
+  __syncthreads();
+  int32_t* out = klist + ((size_t)bh * Cq + i) * S;
+  const int32_t* kp = k_perm + (size_t)bh * S;
+  for (int32_t q = tid; q < L; q += KL_NT) {
+    // last selected cluster whose start is <= q
+    int lo = 0, hi = msel - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (start[mid] <= q) lo = mid; else hi = mid - 1;
+    }
+    out[q] = min(max(kp[min(max(off[cid[lo]] + (q - start[lo]), 0), S - 1)], 0), S - 1);
+  }
+}
+
+// Work items of the attention kernel: (query cluster << 16) | 256-row tile, per head, in cluster
+// order; unused slots -1.
+__global__ void cluster_items_kernel(const int32_t* __restrict__ q_off, int32_t* __restrict__ items, int32_t Cq,
+                                     int32_t per_head, int32_t tile_rows) {
+  const int32_t bh = blockIdx.x;
+  if (threadIdx.x != 0) return;
+  const int32_t* off = q_off + (size_t)bh * (Cq + 1);
+  int32_t* it = items + (size_t)bh * per_head;
+  int32_t n = 0;
+  for (int32_t c = 0; c < Cq; ++c) {
+    const int32_t rows = off[c + 1] - off[c];
+    for (int32_t t = 0; t * tile_rows < rows && n < per_head; ++t) it[n++] = (c << 16) | t;
+  }
+  for (; n < per_head; ++n) it[n] = -1;
+}
+
+// Explicit instantiations, so that the host pass emits every launch stub the launchers use.
+template __global__ void kmeans_assign_kernel<64>(const bf16*, const bf16*, const float*, int32_t*, int32_t, int32_t,
+                                                  int32_t);
+template __global__ void kmeans_assign_kernel<128>(const bf16*, const bf16*, const float*, int32_t*, int32_t, int32_t,
+                                                   int32_t);
+template __global__ void kmeans_update_kernel<64>(const bf16*, const int32_t*, const int32_t*, float*, int32_t, int32_t);
+template __global__ void kmeans_update_kernel<128>(const bf16*, const int32_t*, const int32_t*, float*, int32_t,
+                                                   int32_t);
+
+inline unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }
+
+}  // namespace
+
+int32_t kmeans_cpad(int32_t C) { return (C + AS_BN - 1) / AS_BN * AS_BN; }
+int32_t cluster_nchunk(int32_t S) { return (S + CHUNK - 1) / CHUNK; }
+
+hipError_t launch_kmeans(const KmeansArgs& a, hipStream_t st) {
+  const int32_t Cpad = kmeans_cpad(a.C);
+  const int32_t nchunk = cluster_nchunk(a.S);
+  if (a.init_idx) {
+    kmeans_init_kernel<<<cdiv((int64_t)a.BH * a.C * a.D, 256), 256, 0, st>>>(a.x, a.init_idx, a.cent, a.BH, a.S, a.C,
+                                                                             a.D);
+  }
+  const int32_t nrb = (a.S + AS_BM - 1) / AS_BM;
+  for (int32_t it = 0; it < a.iters; ++it) {
+    kmeans_prep_kernel<<<cdiv((int64_t)a.BH * Cpad, 256), 256, 0, st>>>(a.cent, a.cb, a.hn, a.BH, a.C, Cpad, a.D);
+    if (a.D == 128)
+      kmeans_assign_kernel<128><<<(unsigned)(a.BH * nrb), AS_NT, 0, st>>>(a.x, a.cb, a.hn, a.labels, a.S, Cpad, nrb);
+    else
+      kmeans_assign_kernel<64><<<(unsigned)(a.BH * nrb), AS_NT, 0, st>>>(a.x, a.cb, a.hn, a.labels, a.S, Cpad, nrb);
+    const dim3 g2((unsigned)nchunk, (unsigned)a.BH);
+    cluster_hist_kernel<<<g2, 256, a.C * sizeof(int32_t), st>>>(a.labels, a.counts, a.S, a.C, nchunk);
+    cluster_scan_kernel<<<(unsigned)a.BH, SCAN_NT, 0, st>>>(a.counts, a.offsets, a.S, a.C, nchunk);
+    cluster_scatter_kernel<<<g2, 64, a.C * sizeof(int32_t), st>>>(a.labels, a.counts, a.perm, a.S, a.C, nchunk);
+    const dim3 g3((unsigned)a.C, (unsigned)a.BH);
+    if (a.D == 128)
+      kmeans_update_kernel<128><<<g3, 256, 0, st>>>(a.x, a.perm, a.offsets, a.cent, a.S, a.C);
+    else
+      kmeans_update_kernel<64><<<g3, 256, 0, st>>>(a.x, a.perm, a.offsets, a.cent, a.S, a.C);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_centroid_topp(const ToppArgs& a, hipStream_t st) {
+  const dim3 g((unsigned)a.Cq, (unsigned)a.BH);
+  centroid_topp_kernel<<<g, TP_NT, 0, st>>>(a.cq, a.ck, a.k_off, a.sel, a.Cq, a.Ck, a.D, a.scale, a.p);
+  return hipGetLastError();
+}
+
+hipError_t launch_cluster_lists(const ClusterListArgs& a, hipStream_t st) {
+  const dim3 g((unsigned)a.Cq, (unsigned)a.BH);
+  cluster_keylist_kernel<<<g, KL_NT, 0, st>>>(a.sel, a.k_perm, a.k_off, a.klist, a.klen, a.S, a.Cq, a.Ck);
+  cluster_items_kernel<<<(unsigned)a.BH, 64, 0, st>>>(a.q_off, a.items, a.Cq, a.items_per_head, a.tile_rows);
+  return hipGetLastError();
+}
+
+}  // namespace svg

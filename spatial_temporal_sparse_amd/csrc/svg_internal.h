@@ -151,6 +151,60 @@ struct ProfilePlan {
 };
 ProfilePlan profile_plan(int32_t BH, int32_t S, int32_t D, int32_t n_q);
 
+// ------------------------------------------------------------------------------------------
+// Semantic clustering path
+// ------------------------------------------------------------------------------------------
+struct KmeansArgs {
+  const bf16* x;              // [BH][S][D] rows to cluster
+  const int32_t* init_idx;    // [C] cold-start token indices, or null: start from cent
+  float* cent;                // [BH][C][D] centroids, in and out
+  int32_t* labels;            // [BH][S] cluster of each row (last assignment)
+  int32_t* perm;              // [BH][S] tokens sorted by cluster (stable)
+  int32_t* offsets;           // [BH][C+1] first sorted position of each cluster
+  bf16* cb;                   // workspace [BH][Cpad][D] bf16 centroids
+  float* hn;                  // workspace [BH][Cpad] half squared norms
+  int32_t* counts;            // workspace [BH][nchunk][C]
+  int32_t BH, S, D, C, iters;
+};
+int32_t kmeans_cpad(int32_t C);
+int32_t cluster_nchunk(int32_t S);
+hipError_t launch_kmeans(const KmeansArgs& a, hipStream_t st);
+
+struct ToppArgs {
+  const float *cq, *ck;       // [BH][Cq][D], [BH][Ck][D]
+  const int32_t* k_off;       // [BH][Ck+1]
+  uint8_t* sel;               // [BH][Cq][Ck]
+  int32_t BH, Cq, Ck, D;
+  double scale, p;
+};
+constexpr int TOPP_MAX_CK = 1024;
+hipError_t launch_centroid_topp(const ToppArgs& a, hipStream_t st);
+
+// Query rows of one attention workgroup in the clustering path (one query cluster's rows).
+constexpr int CLUSTER_TILE_ROWS = 256;
+inline int32_t cluster_items_per_head(int32_t S, int32_t Cq) {
+  return (S + CLUSTER_TILE_ROWS - 1) / CLUSTER_TILE_ROWS + Cq;
+}
+
+struct ClusterListArgs {
+  const uint8_t* sel;
+  const int32_t *k_perm, *k_off, *q_off;
+  int32_t* klist;             // [BH][Cq][S] token rows of each query cluster's keys
+  int32_t* klen;              // [BH][Cq]
+  int32_t* items;             // [BH][items_per_head]
+  int32_t BH, S, Cq, Ck, items_per_head, tile_rows;
+};
+hipError_t launch_cluster_lists(const ClusterListArgs& a, hipStream_t st);
+
+struct ClusterAttnArgs {
+  const bf16 *q, *k, *v;
+  bf16* o;
+  const int32_t *q_perm, *q_off, *klist, *klen, *items;
+  int32_t BH, S, D, Cq, items_per_head;
+  float scale;
+};
+hipError_t launch_cluster_attention(const ClusterAttnArgs& a, hipStream_t st);
+
 constexpr int ATTN_BM = 128;
 constexpr int ATTN_BN = 64;
 

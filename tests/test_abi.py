@@ -30,7 +30,8 @@ def test_header_declares_the_path():
     names = _declared_functions()
     for n in ("svg_qknorm_rope", "svg_profile_heads", "svg_permute", "svg_unpermute", "svg_build_block_mask",
               "svg_sparse_attn", "svg_dense_attn", "svg_layer", "svg_dense_step", "svg_workspace_bytes",
-              "svg_tile_shape", "svg_status_string", "svg_last_error"):
+              "svg_tile_shape", "svg_status_string", "svg_last_error", "svg_kmeans", "svg_centroid_topp",
+              "svg_cluster_attn"):
         assert n in names
 
 
@@ -155,3 +156,44 @@ def test_binding_rejects_host_tensors(svg):
         svg.permute(x, 4, 8, 8)
     with pytest.raises(ValueError):
         svg.geometry(x, 4, 8, 9)
+
+
+def test_clustering_workspace_sizes(svg):
+    g = svg.Geom(1, 24, 33, 45, 80, 128)
+    S = 33 * 45 * 80
+    km = svg.workspace_bytes(svg.OP_KMEANS, g, 512)
+    # bf16 centroids + half norms + per-chunk counts, each rounded up to 256 bytes
+    want = 24 * 512 * 128 * 2 + 24 * 512 * 4 + -(-(24 * (-(-S // 1024)) * 512 * 4) // 256) * 256
+    assert km == want
+    assert svg.workspace_bytes(svg.OP_KMEANS, g, 0) == 0
+    assert svg.workspace_bytes(svg.OP_KMEANS, g, 4097) == 0
+    ca = svg.workspace_bytes(svg.OP_CLUSTER_ATTN, g, 128)
+    assert ca >= 24 * 128 * S * 4                                      # one key list per query cluster
+    assert svg.workspace_bytes(svg.OP_CLUSTER_ATTN, g, 0) == 0
+
+
+def test_clustering_argument_checks(svg):
+    L = svg.lib
+    good = svg.Geom(1, 2, 4, 8, 8, 64)
+    F2 = ctypes.c_void_p(0x200000)
+    big_ws = 1 << 30
+    # cluster count out of range, iterations out of range, workspace missing
+    assert L.svg_kmeans(FAKE, good, 0, 3, None, FAKE, FAKE, FAKE, FAKE, FAKE, big_ws, None) == -1
+    assert L.svg_kmeans(FAKE, good, 257, 3, None, FAKE, FAKE, FAKE, FAKE, FAKE, big_ws, None) == -1
+    assert L.svg_kmeans(FAKE, good, 16, 0, None, FAKE, FAKE, FAKE, FAKE, FAKE, big_ws, None) == -1
+    assert L.svg_kmeans(FAKE, good, 16, 3, None, FAKE, FAKE, FAKE, FAKE, None, 0, None) == -4
+    assert L.svg_kmeans(FAKE, good, 16, 3, None, FAKE, FAKE, FAKE, FAKE, FAKE, 64, None) == -4
+    assert L.svg_kmeans(None, good, 16, 3, None, FAKE, FAKE, FAKE, FAKE, FAKE, big_ws, None) == -1
+    assert L.svg_kmeans(FAKE, svg.Geom(1, 2, 4, 8, 8, 96), 16, 3, None, FAKE, FAKE, FAKE, FAKE, FAKE, big_ws, None) == -2
+    # top-p: p in (0, 1], at most 1024 key clusters
+    assert L.svg_centroid_topp(FAKE, FAKE, FAKE, good, 8, 16, 0.125, 0.0, FAKE, None) == -1
+    assert L.svg_centroid_topp(FAKE, FAKE, FAKE, good, 8, 16, 0.125, 1.5, FAKE, None) == -1
+    assert L.svg_centroid_topp(FAKE, FAKE, FAKE, svg.Geom(1, 2, 40, 8, 8, 64), 8, 1025, 0.125, 0.9, FAKE, None) == -1
+    assert L.svg_centroid_topp(FAKE, FAKE, FAKE, good, 8, 16, -1.0, 0.9, FAKE, None) == -1
+    # cluster attention: cluster counts and workspace
+    assert L.svg_cluster_attn(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, good, 0, 16, 0.125, F2, FAKE, big_ws,
+                              None) == -1
+    assert L.svg_cluster_attn(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, good, 8, 16, 0.125, F2, None, 0,
+                              None) == -4
+    assert L.svg_cluster_attn(FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, good, 8, 16, 0.125, F2, FAKE, big_ws,
+                              None) == -1
