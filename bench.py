@@ -47,9 +47,11 @@ def parse():
                     help="layout transformation of temporal heads inside the attention kernel, or as separate "
                          "permute / unpermute passes")
     ap.add_argument("--no-compare", action="store_true", help="do not also time the other layout")
-    ap.add_argument("--workload", choices=("hunyuan720p_step", "cogvideox", "wan"), default="hunyuan720p_step",
+    ap.add_argument("--workload", choices=("hunyuan720p_step", "cogvideox", "wan", "hunyuan720p_svg2"),
+                    default="hunyuan720p_step",
                     help="token grid of the step (default: the HunyuanVideo-720p layer the headline is quoted on; "
-                         "the others are the CogVideoX-like D=64 and the Wan-like grids)")
+                         "cogvideox and wan are the CogVideoX-like D=64 and the Wan-like grids; hunyuan720p_svg2 "
+                         "times the semantic clustering path instead, on the 720p grid)")
     ap.add_argument("--denoise", type=int, default=0, metavar="N",
                     help="instead: time the attention layers of an N-step denoising loop through the step driver "
                          "(dense attention for the first quarter of the steps, then profiling + sparse attention), "
@@ -223,6 +225,160 @@ def denoise(args):
     print(json.dumps(res), flush=True)
 
 
+def cluster_flops(cq, ck, sel, D, tile_rows, tile_keys):
+    """(token-level FLOPs, computed-tile FLOPs, mean density) of one clustering-path layer.
+
+    Token level: 4*D per query and key of its selected clusters.  Computed tiles: every query
+    cluster runs ceil(n/256) tiles of 256 rows over ceil(L/64) key tiles of 64.
+    """
+    import torch
+    nq = (cq.offsets[..., 1:] - cq.offsets[..., :-1]).double()                # [B, H, Cq]
+    nk = (ck.offsets[..., 1:] - ck.offsets[..., :-1]).double()                # [B, H, Ck]
+    L = torch.einsum("bhij,bhj->bhi", sel.double(), nk)                      # keys per query cluster
+    tok = 4.0 * D * float((nq * L).sum())
+    tiles = torch.ceil(nq / tile_rows) * tile_rows * torch.ceil(L / tile_keys) * tile_keys
+    S = nq.sum(dim=-1)                                                      # [B, H]
+    density = float(((nq * L).sum(dim=-1) / (S * S)).mean())
+    return tok, 4.0 * D * float(tiles.sum()), density
+
+
+def cluster_cpu_baseline(q, k, v, lq, lk, sel, D):
+    """The fp64 oracle's attention over the selected clusters for 4096 sampled query rows of one
+    head of the layer (given the GPU's clusters and selection); token-level FLOPs / wall time."""
+    import numpy as np
+    import oracle.svg2_oracle as O2
+    try:
+        import threadpoolctl
+        threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    f64 = lambda t: t.detach().cpu().double().numpy()
+    S = q.shape[2]
+    rows = np.sort(np.random.default_rng(321).choice(S, 4096, replace=False))
+    qh, kh, vh = f64(q[0, 0]), f64(k[0, 0]), f64(v[0, 0])
+    lqh, lkh = lq[0, 0].cpu().numpy(), lk[0, 0].cpu().numpy()
+    s = sel[0, 0].cpu().numpy().astype(bool)
+    t0 = time.perf_counter()
+    O2.semantic_attention_rows(qh, kh, vh, rows, lqh, lkh, s, 1.0 / math.sqrt(D))
+    el = time.perf_counter() - t0
+    pairs = float(O2.semantic_mask(lqh[rows], lkh, s).sum())
+    return {"value": 4.0 * D * pairs / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 numpy oracle, attention over the selected clusters of 4096 sampled query rows of one "
+                      f"head (S={S}, D={D}) given the GPU's clusters and selection; token-level FLOPs",
+            "seconds": round(el, 2)}
+
+
+def cluster_bench(args):
+    """The semantic clustering path at the 720p grid: per layer, k-means of Q and K warm-started
+    from the previous step's centroids, centroid top-p selection, attention over the selected
+    clusters.  Steps cycle over the layers; each layer keeps its own centroid cache."""
+    import numpy as np
+    import torch
+
+    import spatial_temporal_sparse_amd as svg
+    from workloads import SEMANTIC_WORKLOADS, init_token_indices, make_qkv_semantic
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = SEMANTIC_WORKLOADS[args.workload]
+    g = wl.geom
+    L = max(1, min(args.layers, 2))
+    log(f"[bench] clustering path: {L} layers of {g}, Cq={wl.Cq} Ck={wl.Ck} p={wl.p} iters={wl.iters}")
+    layers = []
+    for l in range(L):
+        q, k, v = make_qkv_semantic(wl, device="cuda", step=l)
+        iq = torch.from_numpy(init_token_indices(g.S, wl.Cq, wl.seed + 10 * l)).to(dev)
+        ik = torch.from_numpy(init_token_indices(g.S, wl.Ck, wl.seed + 10 * l + 1)).to(dev)
+        layer = svg.ClusterLayer(q, g.F, g.HH, g.WW, wl.Cq, wl.Ck, wl.p, wl.iters, iq, ik)
+        layers.append((q, k, v, layer))
+    F, HH, WW = g.F, g.HH, g.WW
+
+    def step(l, ev=None):
+        q, k, v, ly = layers[l]
+        if ev is not None:
+            ev[0].record()
+        svg.kmeans(q, F, HH, WW, wl.Cq, wl.iters, init_idx=None if ly.warm else ly.init_q, out=ly.cq, ws=ly.ws_km)
+        if ev is not None:
+            ev[1].record()
+        svg.kmeans(k, F, HH, WW, wl.Ck, wl.iters, init_idx=None if ly.warm else ly.init_k, out=ly.ck, ws=ly.ws_km)
+        if ev is not None:
+            ev[2].record()
+        svg.centroid_topp(ly.cq, ly.ck, F, HH, WW, wl.p, ly.scale, sel=ly.sel)
+        if ev is not None:
+            ev[3].record()
+        svg.cluster_attn(q, k, v, ly.cq, ly.ck, ly.sel, F, HH, WW, ly.scale, o=ly.o, ws=ly.ws_attn)
+        if ev is not None:
+            ev[4].record()
+        ly.warm = True
+
+    for i in range(max(args.warmup, 2 * L)):      # cold start, then warm steps
+        step(i % L)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done; timing {args.steps} steps")
+    names = ["kmeans_q", "kmeans_k", "centroid_topp", "cluster_attn"]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i % L, evs[i])
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    st = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(4)] for i in range(args.steps)])
+    stage_ms = {n: float(st[:, j].mean()) for j, n in enumerate(names)}
+    fl = [cluster_flops(ly.cq, ly.ck, ly.sel, g.D, 256, 64) for (_, _, _, ly) in layers]
+    tok = np.array([fl[i % L][0] for i in range(args.steps)])
+    tile = np.array([fl[i % L][1] for i in range(args.steps)])
+    density = float(np.mean([f[2] for f in fl]))
+    attn_tflops = float(np.mean(tile / (st[:, 3] * 1e-3)) / 1e12)
+    tok_tflops = float(np.mean(tok / (st[:, 3] * 1e-3)) / 1e12)
+    BH, S, D = g.B * g.H, g.S, g.D
+    # k-means: the assignment products (2*D per row and padded centroid) and one read of the rows
+    cpad = lambda C: -(-C // 64) * 64
+    km_flops = {n: 2.0 * BH * S * cpad(C) * D * wl.iters for n, C in (("kmeans_q", wl.Cq), ("kmeans_k", wl.Ck))}
+    # the same attention kernel run dense, for the speedup
+    q, k, v, ly = layers[0]
+    od = torch.empty_like(q)
+    svg.dense_attn(q, k, v, F, HH, WW, o=od)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    svg.dense_attn(q, k, v, F, HH, WW, o=od)
+    e1.record()
+    torch.cuda.synchronize()
+    dense_ms = e0.elapsed_time(e1)
+    log(f"[bench] {ms_per_step:.3f} ms/step; stages {json.dumps({k_: round(v_, 4) for k_, v_ in stage_ms.items()})}")
+    result = {
+        "metric": "cluster-attn ms/layer + effective TFLOP/s (% bf16 MFMA peak), 720p shape, semantic clustering",
+        "value": round(float(np.mean(tok)) / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{wl.name}: one layer (k-means of Q and K warm-started from the previous step's "
+                               f"centroids, {wl.iters} iterations each; centroid top-p; attention over the selected "
+                               f"clusters) over {L} layers of fresh inputs",
+                   "B": g.B, "H": g.H, "F": g.F, "HH": g.HH, "WW": g.WW, "S": S, "D": D, "Cq": wl.Cq, "Ck": wl.Ck,
+                   "p": wl.p, "iters": wl.iters, "n_classes": wl.n_classes, "layers": L,
+                   "parallelism": "single GPU"},
+        "density": round(density, 4),
+        "token_tflop_per_layer": round(float(tok.mean()) / 1e12, 4),
+        "tile_tflop_per_layer": round(float(tile.mean()) / 1e12, 4),
+        "cluster_attn_ms": round(stage_ms["cluster_attn"], 4),
+        "cluster_attn_tflops_tile": round(attn_tflops, 2),
+        "cluster_attn_tflops_token": round(tok_tflops, 2),
+        "kmeans_tflops": {n: round(km_flops[n] / (stage_ms[n] * 1e-3) / 1e12, 2) for n in km_flops},
+        "dense_attn_ms": round(dense_ms, 3),
+        "speedup_vs_dense_kernel": round(dense_ms / stage_ms["cluster_attn"], 3),
+        "speedup_vs_dense_step": round(dense_ms / ms_per_step, 3),
+        "stage_ms": {k_: round(v_, 4) for k_, v_ in stage_ms.items()},
+        "roofline": {"bound": "mfma", "kernel": f"cluster_attn_kernel<{D}>", "achieved": round(attn_tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None,
+                     "note": "computed-tile FLOPs over the svg_cluster_attn call (key lists + attention kernel)"},
+    }
+    log("[bench] timing the CPU oracle on a bounded sample")
+    result["cpu_baseline"] = cluster_cpu_baseline(q, k, v, ly.cq.labels, ly.ck.labels, ly.sel, D)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -238,6 +394,9 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards over heads with no "
               f"exchange, so per-GPU throughput is the one-GPU figure.", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "hunyuan720p_svg2":
+        cluster_bench(args)
+        return
     import numpy as np
     import torch
 

@@ -26,28 +26,25 @@ constexpr int AS_BM = 128;     // rows per assignment workgroup (4 wavefronts x 
 constexpr int AS_BN = 64;      // centroids per LDS tile
 constexpr int AS_NT = 256;
 
-// Rounds every centroid to bf16 and stores half its squared norm (of the rounded values);
-// padding centroids past C get +inf, so that they never win.
-__global__ void kmeans_prep_kernel(const float* __restrict__ cent, bf16* __restrict__ cb, float* __restrict__ hn,
-                                   int32_t BH, int32_t C, int32_t Cpad, int32_t D) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+// Rounds every centroid to bf16 and stores half its squared norm (of the rounded values), one
+// wavefront per centroid; padding centroids past C get +inf, so that they never win.
+__global__ __launch_bounds__(256) void kmeans_prep_kernel(const float* __restrict__ cent, bf16* __restrict__ cb,
+                                                          float* __restrict__ hn, int32_t BH, int32_t C, int32_t Cpad,
+                                                          int32_t D) {
+  const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   if (i >= (int64_t)BH * Cpad) return;
   const int32_t bh = (int32_t)(i / Cpad), c = (int32_t)(i - (int64_t)bh * Cpad);
   bf16* dst = cb + i * D;
-  if (c >= C) {
-    for (int d = 0; d < D; ++d) dst[d] = (bf16)0.f;
-    hn[i] = INFINITY;
-    return;
-  }
-  const float* src = cent + ((int64_t)bh * C + c) * D;
   float s = 0.f;
-  for (int d = 0; d < D; ++d) {
-    const bf16 b = (bf16)src[d];
-    dst[d] = b;
-    const float f = (float)b;
+  for (int d = lane; d < D; d += 64) {
+    const bf16 v = c < C ? (bf16)cent[((int64_t)bh * C + c) * D + d] : (bf16)0.f;
+    dst[d] = v;
+    const float f = (float)v;
     s = fmaf(f, f, s);
   }
-  hn[i] = 0.5f * s;
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  if (lane == 0) hn[i] = c < C ? 0.5f * s : INFINITY;
 }
 
 // Cold start: centroid c of every head is the row at token idx[c] (clamped into [0, S)).
@@ -65,8 +62,11 @@ __global__ void kmeans_init_kernel(const bf16* __restrict__ x, const int32_t* __
 
 // Nearest centroid of 128 rows per workgroup.  Wavefront w holds rows 32w..32w+31 as the B
 // operand of v_mfma_f32_32x32x16_bf16 (one row per lane column); tiles of 64 centroids are the
-// A operand from LDS.  The accumulator gives each lane one row and 16 centroids per 32-block, in
-// increasing centroid order, so a strict comparison keeps the lowest index among equals.
+// A operand from LDS, double-buffered: the next tile's global loads are in flight while the
+// current one is multiplied.  The accumulator starts at -|c|^2/2 of its centroid, so it ends at
+// the score x.c - |c|^2/2 itself.  It gives each lane one row and 16 centroids per 32-block in
+// increasing order: a lane takes the tile's maximum, and only when that beats its best so far
+// looks up which centroid gave it (the first one, the lowest index among equals).
 template <int D>
 __global__ __launch_bounds__(AS_NT) void kmeans_assign_kernel(const bf16* __restrict__ x, const bf16* __restrict__ cb,
                                                               const float* __restrict__ hn, int32_t* __restrict__ labels,
@@ -74,8 +74,9 @@ __global__ __launch_bounds__(AS_NT) void kmeans_assign_kernel(const bf16* __rest
   constexpr int NKS = D / 16;
   constexpr int CPR = D / 8;                  // 16-byte chunks per row
   constexpr int RPB = 16 / CPR;               // rows per 256-byte bank period
-  __shared__ __attribute__((aligned(16))) bf16 ct[AS_BN * D];
-  __shared__ float th[AS_BN];
+  constexpr int PER_T = AS_BN * CPR / AS_NT;  // 16-byte chunks each thread moves per tile
+  __shared__ __attribute__((aligned(16))) bf16 ct[2][AS_BN * D];
+  __shared__ __attribute__((aligned(16))) float th[2][AS_BN];
 
   const int32_t bh = blockIdx.x / nrb;
   const int32_t rb = blockIdx.x - bh * nrb;
@@ -91,42 +92,73 @@ __global__ __launch_bounds__(AS_NT) void kmeans_assign_kernel(const bf16* __rest
 #pragma unroll
   for (int s = 0; s < NKS; ++s) xf[s] = *reinterpret_cast<const bf16x8*>(xr + 16 * s + 8 * hh);
 
+  // chunk o = tid + AS_NT * i of a tile: row o / CPR, chunk o % CPR, stored at slot
+  // chunk ^ ((row / RPB) & (CPR - 1)) of its row
+  u32x4 pre[PER_T];
+  float pre_h = 0.f;
+  auto fetch = [&](int32_t c0) {
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const int o = tid + AS_NT * i;
+      pre[i] = *reinterpret_cast<const u32x4*>(cbh + (size_t)(c0 + o / CPR) * D + 8 * (o % CPR));
+    }
+    if (tid < AS_BN) pre_h = -hnh[c0 + tid];
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const int o = tid + AS_NT * i;
+      const int r = o / CPR, q = o % CPR;
+      *reinterpret_cast<u32x4*>(&ct[buf][r * D + 8 * (q ^ ((r / RPB) & (CPR - 1)))]) = pre[i];
+    }
+    if (tid < AS_BN) th[buf][tid] = pre_h;
+  };
+
   float best = -INFINITY;
   int32_t best_c = 0;
-  for (int32_t c0 = 0; c0 < Cpad; c0 += AS_BN) {
-    __syncthreads();
-    // 16-byte chunk q of tile row r goes to slot q ^ ((r / RPB) & (CPR - 1)) of the row
-    for (int o = tid; o < AS_BN * CPR; o += AS_NT) {
-      const int r = o / CPR, q = o % CPR;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(cbh + (size_t)(c0 + r) * D + 8 * q);
-      *reinterpret_cast<u32x4*>(ct + r * D + 8 * (q ^ ((r / RPB) & (CPR - 1)))) = v;
-    }
-    if (tid < AS_BN) th[tid] = hnh[c0 + tid];
-    __syncthreads();
+  const int nt = Cpad / AS_BN;
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  for (int t = 0; t < nt; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < nt) fetch((t + 1) * AS_BN);
     f32x16 acc[2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[blk][r] = 0.f;
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 h4 = *reinterpret_cast<const f32x4*>(&th[buf][blk * 32 + 8 * g4 + 4 * hh]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[blk][4 * g4 + e] = h4[e];
+      }
 #pragma unroll
     for (int s = 0; s < NKS; ++s)
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
         const int r = blk * 32 + l32;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ct + r * D + 8 * ((2 * s + hh) ^ ((r / RPB) & (CPR - 1))));
+        const bf16x8 a =
+            *reinterpret_cast<const bf16x8*>(&ct[buf][r * D + 8 * ((2 * s + hh) ^ ((r / RPB) & (CPR - 1)))]);
         acc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, xf[s], acc[blk], 0, 0, 0);
       }
+    float m = acc[0][0];
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
+    for (int r = 1; r < 16; ++r) m = fmaxf(m, acc[0][r]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int cl = blk * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-        const float sc = acc[blk][r] - th[cl];
-        if (sc > best) {
-          best = sc;
-          best_c = c0 + cl;
-        }
-      }
+    for (int r = 0; r < 16; ++r) m = fmaxf(m, acc[1][r]);
+    if (m > best) {
+      // the first centroid of the tile that reaches m: scan from the last one down
+      int cl = 0;
+#pragma unroll
+      for (int blk = 1; blk >= 0; --blk)
+#pragma unroll
+        for (int r = 15; r >= 0; --r)
+          if (acc[blk][r] == m) cl = blk * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+      best = m;
+      best_c = t * AS_BN + cl;
+    }
+    if (t + 1 < nt) stash(buf ^ 1);
+    __syncthreads();
   }
   // the two lane halves hold interleaved centroids: larger score wins, then lower index
   const auto rb2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(best), __float_as_uint(best), false, false);
@@ -137,27 +169,29 @@ __global__ __launch_bounds__(AS_NT) void kmeans_assign_kernel(const bf16* __rest
   if (hh == 0 && row < S) labels[(size_t)bh * S + row] = best_c;
 }
 
-constexpr int CHUNK = 1024;     // tokens per counting-sort chunk
+constexpr int CHUNK = 256;      // tokens per counting-sort chunk (one wavefront's share)
 
 // counts[bh][chunk][c]: tokens of the chunk in cluster c.
-__global__ void cluster_hist_kernel(const int32_t* __restrict__ labels, int32_t* __restrict__ counts, int32_t S,
-                                    int32_t C, int32_t nchunk) {
+__global__ __launch_bounds__(CHUNK) void cluster_hist_kernel(const int32_t* __restrict__ labels,
+                                                             int32_t* __restrict__ counts, int32_t S, int32_t C,
+                                                             int32_t nchunk) {
   extern __shared__ int32_t cnt[];
   const int32_t chunk = blockIdx.x, bh = blockIdx.y;
-  for (int c = threadIdx.x; c < C; c += blockDim.x) cnt[c] = 0;
+  for (int c = threadIdx.x; c < C; c += CHUNK) cnt[c] = 0;
   __syncthreads();
-  const int32_t t0 = chunk * CHUNK, t1 = min(t0 + CHUNK, S);
-  for (int32_t t = t0 + threadIdx.x; t < t1; t += blockDim.x)
-    atomicAdd(&cnt[min(max(labels[(size_t)bh * S + t], 0), C - 1)], 1);
+  const int32_t t = chunk * CHUNK + threadIdx.x;
+  if (t < S) atomicAdd(&cnt[min(max(labels[(size_t)bh * S + t], 0), C - 1)], 1);
   __syncthreads();
   int32_t* out = counts + ((size_t)bh * nchunk + chunk) * C;
-  for (int c = threadIdx.x; c < C; c += blockDim.x) out[c] = cnt[c];
+  for (int c = threadIdx.x; c < C; c += CHUNK) out[c] = cnt[c];
 }
 
-// In place: counts[bh][chunk][c] -> first sorted position of chunk's tokens of cluster c
+// In place: counts[bh][chunk][c] -> first sorted position of the chunk's tokens of cluster c
 // (clusters in index order, chunks in order inside a cluster); offsets[bh][c] = start of
-// cluster c, offsets[bh][C] = S.
+// cluster c, offsets[bh][C] = S.  Thread c walks cluster c's counts down the chunks (adjacent
+// threads read adjacent words), several loads in flight at a time.
 constexpr int SCAN_NT = 1024;
+constexpr int SCAN_UNR = 8;
 __global__ __launch_bounds__(SCAN_NT) void cluster_scan_kernel(int32_t* __restrict__ counts,
                                                                int32_t* __restrict__ offsets, int32_t S, int32_t C,
                                                                int32_t nchunk) {
@@ -165,29 +199,54 @@ __global__ __launch_bounds__(SCAN_NT) void cluster_scan_kernel(int32_t* __restri
   const int32_t bh = blockIdx.x;
   const int tid = threadIdx.x;
   int32_t* cnt = counts + (size_t)bh * nchunk * C;
-  // thread tid owns clusters [tid * per, (tid + 1) * per)
-  const int per = (C + SCAN_NT - 1) / SCAN_NT;
-  const int c_lo = min(tid * per, C), c_hi = min(c_lo + per, C);
-  int32_t own = 0;
-  for (int c = c_lo; c < c_hi; ++c)
-    for (int32_t k = 0; k < nchunk; ++k) own += cnt[(size_t)k * C + c];
-  part[tid] = own;
-  __syncthreads();
-  // inclusive scan of the per-thread totals (Hillis-Steele)
-  for (int o = 1; o < SCAN_NT; o <<= 1) {
-    const int32_t v = tid >= o ? part[tid - o] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
-  }
-  int32_t run = part[tid] - own;
+  // thread tid owns clusters tid, tid + SCAN_NT, ... (at most C / SCAN_NT + 1 of them); their
+  // totals are scanned in cluster order below, one pass per owned cluster
   int32_t* off = offsets + (size_t)bh * (C + 1);
-  for (int c = c_lo; c < c_hi; ++c) {
-    off[c] = run;
-    for (int32_t k = 0; k < nchunk; ++k) {
-      const int32_t n = cnt[(size_t)k * C + c];
-      cnt[(size_t)k * C + c] = run;
-      run += n;
+  int32_t carry = 0;
+  for (int c0 = 0; c0 < C; c0 += SCAN_NT) {
+    const int c = c0 + tid;
+    int32_t own = 0;
+    if (c < C) {
+      int32_t k = 0;
+      for (; k + SCAN_UNR <= nchunk; k += SCAN_UNR) {
+        int32_t v[SCAN_UNR];
+#pragma unroll
+        for (int e = 0; e < SCAN_UNR; ++e) v[e] = cnt[(size_t)(k + e) * C + c];
+#pragma unroll
+        for (int e = 0; e < SCAN_UNR; ++e) own += v[e];
+      }
+      for (; k < nchunk; ++k) own += cnt[(size_t)k * C + c];
+    }
+    __syncthreads();
+    part[tid] = own;
+    __syncthreads();
+    // inclusive scan of the totals of clusters c0 .. c0 + SCAN_NT - 1 (Hillis-Steele)
+    for (int o = 1; o < SCAN_NT; o <<= 1) {
+      const int32_t w = tid >= o ? part[tid - o] : 0;
+      __syncthreads();
+      part[tid] += w;
+      __syncthreads();
+    }
+    int32_t run = carry + part[tid] - own;
+    carry += part[SCAN_NT - 1];
+    if (c < C) {
+      off[c] = run;
+      int32_t k = 0;
+      for (; k + SCAN_UNR <= nchunk; k += SCAN_UNR) {
+        int32_t v[SCAN_UNR];
+#pragma unroll
+        for (int e = 0; e < SCAN_UNR; ++e) v[e] = cnt[(size_t)(k + e) * C + c];
+#pragma unroll
+        for (int e = 0; e < SCAN_UNR; ++e) {
+          cnt[(size_t)(k + e) * C + c] = run;
+          run += v[e];
+        }
+      }
+      for (; k < nchunk; ++k) {
+        const int32_t n = cnt[(size_t)k * C + c];
+        cnt[(size_t)k * C + c] = run;
+        run += n;
+      }
     }
   }
   if (tid == 0) off[C] = S;
@@ -229,34 +288,57 @@ __global__ __launch_bounds__(64) void cluster_scatter_kernel(const int32_t* __re
   }
 }
 
-// Mean of each cluster's rows in fp64 (rows in sorted order, four wavefronts interleaved, a
-// fixed reduction order); an empty cluster keeps its centroid.
+// Mean of each cluster's rows in fp64, one workgroup per (cluster, head).  A row is read as
+// 16-byte pieces by D/8 lanes, so one wavefront load covers 64*8/D rows ("slots"); each
+// wavefront keeps UNR such loads in flight.  Row j of the cluster goes to a fixed (wavefront,
+// unroll step, slot), and the partial sums are combined in a fixed order, so the result does
+// not depend on timing.  An empty cluster keeps its centroid.
+constexpr int UP_NT = 256;
+constexpr int UP_UNR = 4;
 template <int D>
-__global__ __launch_bounds__(256) void kmeans_update_kernel(const bf16* __restrict__ x, const int32_t* __restrict__ perm,
-                                                            const int32_t* __restrict__ offsets,
-                                                            float* __restrict__ cent, int32_t S, int32_t C) {
-  constexpr int CPL = D / 64;    // columns per lane
-  __shared__ double red[4][D];
+__global__ __launch_bounds__(UP_NT) void kmeans_update_kernel(const bf16* __restrict__ x, const int32_t* __restrict__ perm,
+                                                              const int32_t* __restrict__ offsets,
+                                                              float* __restrict__ cent, int32_t S, int32_t C) {
+  constexpr int LPR = D / 8;                   // lanes per row
+  constexpr int SLOTS = 64 / LPR;              // rows per wavefront load
+  constexpr int NW = UP_NT / 64;
+  constexpr int PER_IT = NW * UP_UNR * SLOTS;  // rows per workgroup iteration
+  __shared__ double red[NW * SLOTS][D];
   const int32_t c = blockIdx.x, bh = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int slot = lane / LPR, piece = lane % LPR;
   const int32_t* off = offsets + (size_t)bh * (C + 1);
   const int32_t j0 = off[c], j1 = off[c + 1];
-  if (j1 == j0) return;
-  const bf16* xh = x + (size_t)bh * S * D;
+  if (j1 <= j0) return;
+  const bf16* xh = x + (size_t)bh * S * D + 8 * piece;
   const int32_t* ph = perm + (size_t)bh * S;
-  double acc[CPL];
+  double acc[8];
 #pragma unroll
-  for (int e = 0; e < CPL; ++e) acc[e] = 0.0;
-  for (int32_t j = j0 + wave; j < j1; j += 4) {
-    const bf16* r = xh + (size_t)min(max(ph[j], 0), S - 1) * D + CPL * lane;
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+  for (int32_t jb = j0; jb < j1; jb += PER_IT) {
+    u32x4 v[UP_UNR];
+    bool ok[UP_UNR];
 #pragma unroll
-    for (int e = 0; e < CPL; ++e) acc[e] += (double)(float)r[e];
+    for (int u = 0; u < UP_UNR; ++u) {
+      const int32_t j = jb + (u * NW + wave) * SLOTS + slot;
+      ok[u] = j < j1;
+      const int32_t t = min(max(ph[min(j, j1 - 1)], 0), S - 1);
+      v[u] = *reinterpret_cast<const u32x4*>(xh + (size_t)t * D);
+    }
+#pragma unroll
+    for (int u = 0; u < UP_UNR; ++u) {
+      if (!ok[u]) continue;
+      const bf16x8 b = __builtin_bit_cast(bf16x8, v[u]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += (double)(float)b[e];
+    }
   }
 #pragma unroll
-  for (int e = 0; e < CPL; ++e) red[wave][CPL * lane + e] = acc[e];
+  for (int e = 0; e < 8; ++e) red[wave * SLOTS + slot][8 * piece + e] = acc[e];
   __syncthreads();
   if (tid < D) {
-    const double s = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+    double s = 0.0;
+    for (int i = 0; i < NW * SLOTS; ++i) s += red[i][tid];
     cent[((size_t)bh * C + c) * D + tid] = (float)(s / (double)(j1 - j0));
   }
 }
@@ -470,20 +552,20 @@ hipError_t launch_kmeans(const KmeansArgs& a, hipStream_t st) {
   }
   const int32_t nrb = (a.S + AS_BM - 1) / AS_BM;
   for (int32_t it = 0; it < a.iters; ++it) {
-    kmeans_prep_kernel<<<cdiv((int64_t)a.BH * Cpad, 256), 256, 0, st>>>(a.cent, a.cb, a.hn, a.BH, a.C, Cpad, a.D);
+    kmeans_prep_kernel<<<cdiv((int64_t)a.BH * Cpad, 4), 256, 0, st>>>(a.cent, a.cb, a.hn, a.BH, a.C, Cpad, a.D);
     if (a.D == 128)
       kmeans_assign_kernel<128><<<(unsigned)(a.BH * nrb), AS_NT, 0, st>>>(a.x, a.cb, a.hn, a.labels, a.S, Cpad, nrb);
     else
       kmeans_assign_kernel<64><<<(unsigned)(a.BH * nrb), AS_NT, 0, st>>>(a.x, a.cb, a.hn, a.labels, a.S, Cpad, nrb);
     const dim3 g2((unsigned)nchunk, (unsigned)a.BH);
-    cluster_hist_kernel<<<g2, 256, a.C * sizeof(int32_t), st>>>(a.labels, a.counts, a.S, a.C, nchunk);
+    cluster_hist_kernel<<<g2, CHUNK, a.C * sizeof(int32_t), st>>>(a.labels, a.counts, a.S, a.C, nchunk);
     cluster_scan_kernel<<<(unsigned)a.BH, SCAN_NT, 0, st>>>(a.counts, a.offsets, a.S, a.C, nchunk);
     cluster_scatter_kernel<<<g2, 64, a.C * sizeof(int32_t), st>>>(a.labels, a.counts, a.perm, a.S, a.C, nchunk);
     const dim3 g3((unsigned)a.C, (unsigned)a.BH);
     if (a.D == 128)
-      kmeans_update_kernel<128><<<g3, 256, 0, st>>>(a.x, a.perm, a.offsets, a.cent, a.S, a.C);
+      kmeans_update_kernel<128><<<g3, UP_NT, 0, st>>>(a.x, a.perm, a.offsets, a.cent, a.S, a.C);
     else
-      kmeans_update_kernel<64><<<g3, 256, 0, st>>>(a.x, a.perm, a.offsets, a.cent, a.S, a.C);
+      kmeans_update_kernel<64><<<g3, UP_NT, 0, st>>>(a.x, a.perm, a.offsets, a.cent, a.S, a.C);
   }
   return hipGetLastError();
 }

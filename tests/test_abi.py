@@ -163,7 +163,7 @@ def test_clustering_workspace_sizes(svg):
     S = 33 * 45 * 80
     km = svg.workspace_bytes(svg.OP_KMEANS, g, 512)
     # bf16 centroids + half norms + per-chunk counts, each rounded up to 256 bytes
-    want = 24 * 512 * 128 * 2 + 24 * 512 * 4 + -(-(24 * (-(-S // 1024)) * 512 * 4) // 256) * 256
+    want = 24 * 512 * 128 * 2 + 24 * 512 * 4 + -(-(24 * (-(-S // 256)) * 512 * 4) // 256) * 256
     assert km == want
     assert svg.workspace_bytes(svg.OP_KMEANS, g, 0) == 0
     assert svg.workspace_bytes(svg.OP_KMEANS, g, 4097) == 0
