@@ -31,6 +31,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_hunyuan720p_traffic.json")
+CLUSTER_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "cluster_attn_hunyuan720p_svg2_traffic.json")
 
 
 def log(msg):
@@ -108,11 +109,11 @@ def kernel_sha():
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
+def measured_traffic(path=TRAFFIC_FILE):
     """HBM bytes per launch of the attention kernel from the committed counter runs, if they
     were taken on the current kernel source; else None."""
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(path) as fh:
             t = json.load(fh)
     except (OSError, ValueError):
         return None
@@ -371,7 +372,7 @@ def cluster_bench(args):
         "stage_ms": {k_: round(v_, 4) for k_, v_ in stage_ms.items()},
         "roofline": {"bound": "mfma", "kernel": f"cluster_attn_kernel<{D}>", "achieved": round(attn_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None,
+                     "traffic": measured_traffic(CLUSTER_TRAFFIC_FILE),
                      "note": "computed-tile FLOPs over the svg_cluster_attn call (key lists + attention kernel)"},
     }
     log("[bench] timing the CPU oracle on a bounded sample")
