@@ -256,3 +256,50 @@ def test_full_720p_sampled(gpu):
         dens.append(sum(nq[i] * nk[s[i]].sum() for i in range(wl.Cq)) / g.S ** 2)
     note(f"720p density {np.mean(dens):.4f} (min {np.min(dens):.4f}, max {np.max(dens):.4f})")
     assert 0.0 < np.mean(dens) < 0.5
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_one_cluster_each_is_dense_attention(gpu, D):
+    """C_q = C_k = 1: every query attends every key in token order, the dense kernel's own
+    schedule, so the output equals svg_dense_attn bit for bit."""
+    g = Geometry(1, 2, 3, 9, 11, D)
+    wl = _semantic("one_cluster", g, 3, 1, 1, 0.5, 2, 35)
+    note(f"one cluster each, D={D}")
+    q, k, v, iq, ik = _inputs(wl)
+    cq = gpu.kmeans(q, g.F, g.HH, g.WW, 1, 2, init_idx=iq)
+    ck = gpu.kmeans(k, g.F, g.HH, g.WW, 1, 2, init_idx=ik)
+    sel = gpu.centroid_topp(cq, ck, g.F, g.HH, g.WW, 0.5)
+    o = gpu.cluster_attn(q, k, v, cq, ck, sel, g.F, g.HH, g.WW)
+    od = gpu.dense_attn(q, k, v, g.F, g.HH, g.WW)
+    torch.cuda.synchronize()
+    assert (sel == 1).all()
+    assert torch.equal(cq.perm[0, 0].cpu(), torch.arange(g.S, dtype=torch.int32))
+    assert torch.equal(o, od)
+
+
+def test_one_token_per_cluster(gpu):
+    """C = S: every token is its own cluster, so the estimated shares are the exact attention
+    weights of each query, and top-p keeps each query's top-p keys."""
+    g = Geometry(1, 2, 4, 7, 9, 64)
+    wl = _semantic("token_clusters", g, 4, g.S, g.S, 0.6, 1, 36)
+    note("one token per cluster")
+    q, k, v, _, _ = _inputs(wl)
+    every = torch.arange(g.S, dtype=torch.int32, device=DEV)
+    cq = gpu.kmeans(q, g.F, g.HH, g.WW, g.S, 1, init_idx=every)
+    ck = gpu.kmeans(k, g.F, g.HH, g.WW, g.S, 1, init_idx=every)
+    sel = gpu.centroid_topp(cq, ck, g.F, g.HH, g.WW, wl.p)
+    o = gpu.cluster_attn(q, k, v, cq, ck, sel, g.F, g.HH, g.WW)
+    torch.cuda.synchronize()
+    qh, kh, vh, oh = host64(q), host64(k), host64(v), host64(o)
+    sc = 1.0 / np.sqrt(g.D)
+    for h in range(g.H):
+        lq = cq.labels[0, h].cpu().numpy()
+        lk = ck.labels[0, h].cpu().numpy()
+        # distinct random rows: each token is nearest to its own start
+        assert np.array_equal(lq, np.arange(g.S)) and np.array_equal(lk, np.arange(g.S))
+        w = O2.centroid_weights(cq.centroids[0, h].cpu().numpy(), ck.centroids[0, h].cpu().numpy(),
+                                np.ones(g.S), sc)
+        s = sel[0, h].cpu().numpy()
+        _check_topp(w, s, wl.p, f"h{h}")
+        want = O2.semantic_attention(qh[0, h], kh[0, h], vh[0, h], lq, lk, s.astype(bool), sc)
+        assert_close_attn(oh[0, h], want, f"h{h}")
