@@ -10,6 +10,8 @@
  *                 t/topic/12021).
  *   [svg2-gist]   "Sparse VideoGen2: Accelerate Video Generation with Sparse Attention
  *                 via Semantic-Aware Permutation", explainer at gist.science (2505.18875).
+ *   [adaspa]      "Training-free and Adaptive Sparse Attention for Efficient Long Video
+ *                 Generation", the arxivdaily page of arXiv 2502.21079 (its abstract).
  *
  * Conventions shared by every call
  * --------------------------------
@@ -60,6 +62,11 @@ typedef int32_t svg_status;
 #define SVG_OP_LAYER       3
 #define SVG_OP_KMEANS      4   /* n = cluster count C */
 #define SVG_OP_CLUSTER_ATTN 5  /* n = query cluster count Cq */
+#define SVG_OP_BLOCK_ATTN  6   /* n unused */
+
+/* Blocks of the block-sparse path: query rows x keys. */
+#define SVG_BLOCK_Q 256
+#define SVG_BLOCK_K 64
 
 typedef struct {
     int32_t B, H;       /* batch, heads */
@@ -278,6 +285,54 @@ svg_status svg_cluster_attn(const void* q, const void* k, const void* v, const i
                             const int32_t* q_offsets, const int32_t* k_perm, const int32_t* k_offsets,
                             const uint8_t* sel, svg_geom g, int32_t Cq, int32_t Ck, float scale, void* o, void* ws,
                             size_t ws_bytes, void* stream);
+
+/*
+ * ---------------------------------------------------------------------------------------
+ * Head-adaptive block-sparse path with an LSE-cached block search ([adaspa] abstract: a
+ * blockified sparse pattern; a search that uses the log-sum-exp of attention rows cached from
+ * earlier denoising steps; head-adaptive block-sparse attention).  Blocks are SVG_BLOCK_Q
+ * query rows by SVG_BLOCK_K keys in token order, the last ones clipped at S:
+ * nqb = ceil(S / 256) query blocks and nkb = ceil(S / 64) key blocks, nkb <= 4096.
+ * ---------------------------------------------------------------------------------------
+ */
+
+/*
+ * svg_dense_attn_lse -- svg_dense_attn that also writes every row's natural-log log-sum-exp
+ * LSE_q = log sum_k exp(scale q.k) (from the kernel's running max and the row sum of its bf16
+ * weights): the normaliser a later step's block search reuses.
+ * lse: fp32 [B*H][S] out.
+ */
+svg_status svg_dense_attn_lse(const void* q, const void* k, const void* v, svg_geom g, float scale, void* o,
+                              float* lse, void* stream);
+
+/*
+ * svg_block_mass -- the attention mass of every block under a cached normaliser:
+ * mass[i][j] = sum over rows q of query block i and keys k of key block j of
+ * exp(scale q.k - lse[q]) (bf16 products, fp32 accumulation, exponentials and sums).  With the
+ * lse of the same q and k, a block row sums to its row count.
+ * q, k: bf16 [B][H][S][D].  lse: fp32 [B*H][S] (from svg_dense_attn_lse of an earlier step).
+ * mass: fp32 [B*H][nqb][nkb] out.
+ */
+svg_status svg_block_mass(const void* q, const void* k, const float* lse, svg_geom g, float scale, float* mass,
+                          void* stream);
+
+/*
+ * svg_block_select -- the head-adaptive choice: per (b, h) and query block, key blocks in
+ * decreasing mass (ties: lower block first) until their mass reaches coverage times the
+ * block row's total mass (fp64 prefix sums of the fp32 masses); blocks of zero mass are never
+ * chosen.  coverage: (0, 1].  sel: uint8 [B*H][nqb][nkb] out, 1 = chosen.
+ */
+svg_status svg_block_select(const float* mass, svg_geom g, float coverage, uint8_t* sel, void* stream);
+
+/*
+ * svg_block_sparse_attn -- attention of every query to exactly the keys of the key blocks
+ * chosen for its query block (any uint8 [B*H][nqb][nkb] block mask), with the keys of the
+ * chosen blocks gathered into the attention kernel's 64-key tiles.  A query block with no
+ * chosen block leaves its rows unwritten.
+ * o: bf16 [B][H][S][D] out.  ws: >= svg_workspace_bytes(SVG_OP_BLOCK_ATTN, &g, 0) bytes.
+ */
+svg_status svg_block_sparse_attn(const void* q, const void* k, const void* v, const uint8_t* sel, svg_geom g,
+                                 float scale, void* o, void* ws, size_t ws_bytes, void* stream);
 
 /* Bytes of workspace a call needs (0 for an invalid request); n is the sample size n_q for
  * SVG_OP_PROFILE and SVG_OP_LAYER, the cluster count for SVG_OP_KMEANS and SVG_OP_CLUSTER_ATTN. */

@@ -28,6 +28,9 @@ OP_SPARSE_ATTN = 2
 OP_LAYER = 3
 OP_KMEANS = 4
 OP_CLUSTER_ATTN = 5
+OP_BLOCK_ATTN = 6
+BLOCK_Q = 256
+BLOCK_K = 64
 
 _c_i32 = ctypes.c_int32
 _c_vp = ctypes.c_void_p
@@ -70,6 +73,11 @@ _SIGNATURES = {
                                _c_vp]),
     "svg_cluster_attn": (_st, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, Geom, _c_i32, _c_i32,
                               ctypes.c_float, _c_vp, _c_vp, ctypes.c_size_t, _c_vp]),
+    "svg_dense_attn_lse": (_st, [_c_vp, _c_vp, _c_vp, Geom, ctypes.c_float, _c_vp, _c_vp, _c_vp]),
+    "svg_block_mass": (_st, [_c_vp, _c_vp, _c_vp, Geom, ctypes.c_float, _c_vp, _c_vp]),
+    "svg_block_select": (_st, [_c_vp, Geom, ctypes.c_float, _c_vp, _c_vp]),
+    "svg_block_sparse_attn": (_st, [_c_vp, _c_vp, _c_vp, _c_vp, Geom, ctypes.c_float, _c_vp, _c_vp, ctypes.c_size_t,
+                                   _c_vp]),
     "svg_workspace_bytes": (ctypes.c_size_t, [_c_i32, ctypes.POINTER(Geom), _c_i32]),
     "svg_tile_shape": (None, [ctypes.POINTER(_c_i32), ctypes.POINTER(_c_i32)]),
     "svg_status_string": (ctypes.c_char_p, [_c_i32]),
@@ -553,4 +561,76 @@ class ClusterLayer:
                      ws=self.ws_attn)
         self.warm = True
         return self.o
+
+
+# ----------------------------------------------------------------------------------------------
+# Head-adaptive block-sparse path with an LSE-cached block search
+# ----------------------------------------------------------------------------------------------
+def block_grid(S: int) -> Tuple[int, int]:
+    """(query blocks, key blocks) of a sequence of S tokens."""
+    return -(-S // BLOCK_Q), -(-S // BLOCK_K)
+
+
+def dense_attn_lse(q, k, v, F, HH, WW, scale=None, o=None, lse=None):
+    """Dense attention and each row's natural-log log-sum-exp (svg_dense_attn_lse).
+    Returns (o [B, H, S, D] bf16, lse [B, H, S] fp32)."""
+    g = geometry(q, F, HH, WW)
+    shp = _shape(g)
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check_qkv(n, t, shp, device=q.device)
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty(shp[:3], dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_qkv("o", o, shp, device=q.device)
+    _check_qkv("lse", lse, shp[:3], torch.float32, q.device)
+    sc = default_scale(g.D) if scale is None else scale
+    _check(lib.svg_dense_attn_lse(_ptr(q), _ptr(k), _ptr(v), g, float(sc), _ptr(o), _ptr(lse), _stream(q)))
+    return o, lse
+
+
+def block_mass(q, k, lse, F, HH, WW, scale=None, mass=None):
+    """Attention mass of every (256-row, 64-key) block under the cached lse (svg_block_mass).
+    Returns fp32 [B, H, nqb, nkb]."""
+    g = geometry(q, F, HH, WW)
+    shp = _shape(g)
+    _check_qkv("q", q, shp)
+    _check_qkv("k", k, shp, device=q.device)
+    _check_qkv("lse", lse, shp[:3], torch.float32, q.device)
+    nqb, nkb = block_grid(shp[2])
+    mass = torch.empty((g.B, g.H, nqb, nkb), dtype=torch.float32, device=q.device) if mass is None else mass
+    _check_qkv("mass", mass, (g.B, g.H, nqb, nkb), torch.float32, q.device)
+    sc = default_scale(g.D) if scale is None else scale
+    _check(lib.svg_block_mass(_ptr(q), _ptr(k), _ptr(lse), g, float(sc), _ptr(mass), _stream(q)))
+    return mass
+
+
+def block_select(mass, F, HH, WW, D, coverage, sel=None):
+    """Per query block, the fewest key blocks carrying `coverage` of its mass (svg_block_select).
+    Returns uint8 [B, H, nqb, nkb]."""
+    B, H, nqb, nkb = mass.shape
+    g = Geom(B, H, F, HH, WW, D)
+    if block_grid(F * HH * WW) != (nqb, nkb):
+        raise ValueError("mass does not match the block grid of the token grid")
+    _check_qkv("mass", mass, (B, H, nqb, nkb), torch.float32, mass.device)
+    sel = torch.empty((B, H, nqb, nkb), dtype=torch.uint8, device=mass.device) if sel is None else sel
+    _check_qkv("sel", sel, (B, H, nqb, nkb), torch.uint8, mass.device)
+    _check(lib.svg_block_select(_ptr(mass), g, float(coverage), _ptr(sel), _stream(mass)))
+    return sel
+
+
+def block_sparse_attn(q, k, v, sel, F, HH, WW, scale=None, o=None, ws=None):
+    """Attention of each query to the keys of its query block's chosen key blocks
+    (svg_block_sparse_attn).  Returns o [B, H, S, D] bf16."""
+    g = geometry(q, F, HH, WW)
+    shp = _shape(g)
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check_qkv(n, t, shp, device=q.device)
+    nqb, nkb = block_grid(shp[2])
+    _check_qkv("sel", sel, (g.B, g.H, nqb, nkb), torch.uint8, q.device)
+    o = torch.empty_like(q) if o is None else o
+    _check_qkv("o", o, shp, device=q.device)
+    ws = _workspace(OP_BLOCK_ATTN, g, 0, q.device, ws)
+    sc = default_scale(g.D) if scale is None else scale
+    _check(lib.svg_block_sparse_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(sel), g, float(sc), _ptr(o), _ptr(ws),
+                                     ws.numel(), _stream(q)))
+    return o
 

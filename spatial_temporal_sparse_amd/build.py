@@ -18,7 +18,7 @@ OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsvg.so")
 
 SOURCES = ["api.cpp", "permute.hip", "block_mask.hip", "qknorm_rope.hip", "attn_fwd.hip", "profile_heads.hip",
-           "cluster.hip"]
+           "cluster.hip", "block_search.hip"]
 
 ARCH = "gfx950"
 # Packed fp32 VALU forms are disabled for every HIP source on purpose.

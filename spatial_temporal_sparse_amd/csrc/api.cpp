@@ -263,6 +263,7 @@ static void fill_attn(svg::AttnArgs& a, svg_geom g, svg_windows w, float scale) 
   a.divP = svg::make_fastdiv((uint32_t)a.P);
   a.divF = svg::make_fastdiv((uint32_t)g.F);
   a.scale = scale;
+  a.lse = nullptr;
 }
 
 static svg_status svg_sparse_attn_impl(const void* q, const void* k, const void* v, const void* qt, const void* kt,
@@ -538,6 +539,115 @@ SVG_API svg_status svg_cluster_attn(const void* q, const void* k, const void* v,
   return hip_status(svg::launch_cluster_attention(a, (hipStream_t)stream), "svg_cluster_attn");
 }
 
+// ---------------------------------------------------------------------------------------------
+// Block-sparse path with an LSE-cached block search
+// ---------------------------------------------------------------------------------------------
+namespace {
+
+int32_t n_qblocks(const svg_geom& g) { return (geom_S(g) + svg::BLOCK_Q_ROWS - 1) / svg::BLOCK_Q_ROWS; }
+int32_t n_kblocks(const svg_geom& g) { return (geom_S(g) + svg::BLOCK_K_ROWS - 1) / svg::BLOCK_K_ROWS; }
+
+svg_status check_blocks(const svg_geom& g) {
+  if (n_kblocks(g) > svg::BLOCK_MAX_NKB)
+    return fail(SVG_ERR_UNSUPPORTED, "S=%d: more than %d key blocks of %d", geom_S(g), svg::BLOCK_MAX_NKB,
+                svg::BLOCK_K_ROWS);
+  return SVG_OK;
+}
+
+size_t block_ws_bytes(const svg_geom& g) {
+  const size_t rows = (size_t)g.B * g.H * n_qblocks(g);
+  return align_up(rows * n_kblocks(g) * sizeof(int32_t), 256) + align_up(rows * sizeof(int32_t), 256);
+}
+
+}  // namespace
+
+SVG_API svg_status svg_dense_attn_lse(const void* q, const void* k, const void* v, svg_geom g, float scale, void* o,
+                                      float* lse, void* stream) {
+  svg_status s;
+  if ((s = check_geom(g, true)) != SVG_OK) return s;
+  if ((s = check_ptrs({{q, "q"}, {k, "k"}, {v, "v"}, {o, "o"}, {lse, "lse"}})) != SVG_OK) return s;
+  if ((s = check_head_bytes(g)) != SVG_OK) return s;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(SVG_ERR_INVALID, "scale must be finite and > 0");
+  svg::AttnArgs a;
+  a.fused_t = 0;
+  a.q = a.qt = (const svg::bf16*)q;
+  a.k = a.kt = (const svg::bf16*)k;
+  a.v = a.vt = (const svg::bf16*)v;
+  a.o = a.ot = (svg::bf16*)o;
+  a.kind = nullptr;
+  a.order = nullptr;
+  a.force_dense = 1;
+  fill_attn(a, g, svg_windows{0, 0}, scale);
+  a.lse = lse;
+  return hip_status(svg::launch_attention_lse(a, (hipStream_t)stream), "svg_dense_attn_lse");
+}
+
+SVG_API svg_status svg_block_mass(const void* q, const void* k, const float* lse, svg_geom g, float scale, float* mass,
+                                  void* stream) {
+  svg_status s;
+  if ((s = check_geom(g, true)) != SVG_OK) return s;
+  if ((s = check_ptrs({{q, "q"}, {k, "k"}, {lse, "lse"}, {mass, "mass"}})) != SVG_OK) return s;
+  if ((s = check_blocks(g)) != SVG_OK) return s;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(SVG_ERR_INVALID, "scale must be finite and > 0");
+  svg::BlockMassArgs a;
+  a.q = (const svg::bf16*)q;
+  a.k = (const svg::bf16*)k;
+  a.lse = lse;
+  a.mass = mass;
+  a.BH = g.B * g.H;
+  a.S = geom_S(g);
+  a.D = g.D;
+  a.nqb = n_qblocks(g);
+  a.nkb = n_kblocks(g);
+  a.scale = scale;
+  return hip_status(svg::launch_block_mass(a, (hipStream_t)stream), "svg_block_mass");
+}
+
+SVG_API svg_status svg_block_select(const float* mass, svg_geom g, float coverage, uint8_t* sel, void* stream) {
+  svg_status s;
+  if ((s = check_geom(g, true)) != SVG_OK) return s;
+  if ((s = check_ptrs({{mass, "mass"}, {sel, "sel"}})) != SVG_OK) return s;
+  if ((s = check_blocks(g)) != SVG_OK) return s;
+  if (!(coverage > 0.f && coverage <= 1.f)) return fail(SVG_ERR_INVALID, "coverage=%g must lie in (0, 1]", (double)coverage);
+  svg::BlockSelectArgs a;
+  a.mass = mass;
+  a.sel = sel;
+  a.BH = g.B * g.H;
+  a.nqb = n_qblocks(g);
+  a.nkb = n_kblocks(g);
+  a.coverage = (double)coverage;
+  return hip_status(svg::launch_block_select(a, (hipStream_t)stream), "svg_block_select");
+}
+
+SVG_API svg_status svg_block_sparse_attn(const void* q, const void* k, const void* v, const uint8_t* sel, svg_geom g,
+                                         float scale, void* o, void* ws, size_t ws_bytes, void* stream) {
+  svg_status s;
+  if ((s = check_geom(g, true)) != SVG_OK) return s;
+  if ((s = check_ptrs({{q, "q"}, {k, "k"}, {v, "v"}, {sel, "sel"}, {o, "o"}})) != SVG_OK) return s;
+  if ((s = check_head_bytes(g)) != SVG_OK) return s;
+  if ((s = check_blocks(g)) != SVG_OK) return s;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(SVG_ERR_INVALID, "scale must be finite and > 0");
+  const size_t need = block_ws_bytes(g);
+  if ((s = check_ws(ws, ws_bytes, need, "svg_block_sparse_attn")) != SVG_OK) return s;
+  svg::BlockAttnArgs a;
+  a.q = (const svg::bf16*)q;
+  a.k = (const svg::bf16*)k;
+  a.v = (const svg::bf16*)v;
+  a.o = (svg::bf16*)o;
+  a.sel = sel;
+  a.BH = g.B * g.H;
+  a.S = geom_S(g);
+  a.D = g.D;
+  a.nqb = n_qblocks(g);
+  a.nkb = n_kblocks(g);
+  a.blist = (int32_t*)ws;
+  a.blen = (int32_t*)((char*)ws + align_up((size_t)a.BH * a.nqb * a.nkb * sizeof(int32_t), 256));
+  a.scale = scale;
+  if ((s = hip_status(svg::launch_block_lists(a, (hipStream_t)stream), "svg_block_sparse_attn (lists)")) != SVG_OK)
+    return s;
+  return hip_status(svg::launch_block_attention(a, (hipStream_t)stream), "svg_block_sparse_attn");
+}
+
 SVG_API size_t svg_workspace_bytes(int32_t op, const svg_geom* g, int32_t n_q) {
   if (g == nullptr) return 0;
   const bool need_d = true;
@@ -565,6 +675,10 @@ SVG_API size_t svg_workspace_bytes(int32_t op, const svg_geom* g, int32_t n_q) {
     const int32_t S = g->F * g->HH * g->WW;
     if (n_q < 1 || n_q > S || n_q > CLUSTER_MAX_CQ) return 0;
     return cluster_ws(*g, n_q).total;
+  }
+  if (op == SVG_OP_BLOCK_ATTN) {
+    if (n_kblocks(*g) > svg::BLOCK_MAX_NKB) return 0;
+    return block_ws_bytes(*g);
   }
   return 0;
 }

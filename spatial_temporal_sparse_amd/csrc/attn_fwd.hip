@@ -359,6 +359,26 @@ struct ClusterSource {
   }
 };
 
+// BlockSource: one 256-row query block in token order against the keys of its chosen 64-key
+// blocks, every one of which its queries attend.  Blocks are listed in increasing order, so
+// only the last may be the sequence's partial block: list position j is key 64 bl[j / 64] +
+// j % 64.
+struct BlockSource {
+  static constexpr bool kGather = true;
+  const int32_t* bl;           // chosen key blocks, increasing
+  int32_t q0, n, L, S;
+  __device__ __forceinline__ int32_t q_row(int32_t u) const { return q0 + min(u, n - 1); }
+  __device__ __forceinline__ int32_t q_row_in(int32_t u) const { return q0 + u; }
+  __device__ __forceinline__ int32_t kv_row(int32_t j) const {
+    const int32_t jj = min(j, L - 1);
+    return min(bl[jj >> 6] * 64 + (jj & 63), S - 1);
+  }
+  __device__ __forceinline__ void interval(int32_t, int32_t& lo, int32_t& hi) const {
+    lo = 0;
+    hi = L;
+  }
+};
+
 // Copy of one K or V tile into LDS by the four wavefronts of one group (wb = 0..3): per
 // wavefront, PER_WAVE instructions of 1 KB each.  The address is the wavefront-uniform head
 // base plus a 32-bit per-lane offset (the host checks that a head fits in 4 GB).  Every lane
@@ -399,10 +419,13 @@ __device__ __forceinline__ void tile_rows(const Src& src, int32_t k0, int wb, in
 
 // The ping-pong loop of one workgroup: 256 logical query rows from q0 (rows at or past n_rows
 // are computed on clamped inputs and not stored).
-template <int D, class Src>
+// With LSE, each stored row also gets its natural-log log-sum-exp, from the running max and
+// the row sum of the bf16 weights: ln 2 * (m + log2 l), m the max in log2 units of the scaled
+// logits.
+template <int D, class Src, bool LSE = false>
 __device__ __forceinline__ void pp_attention(const Src& src, const bf16* __restrict__ Q, const bf16* __restrict__ K,
                                              const bf16* __restrict__ V, bf16* __restrict__ O, int32_t n_rows,
-                                             int32_t q0, float scale) {
+                                             int32_t q0, float scale, float* __restrict__ lse = nullptr) {
   constexpr int NDB = D / 32;
   constexpr int NKS = D / 16;
   constexpr int PW = CopyPlan<D>::PER_WAVE;
@@ -589,6 +612,10 @@ __device__ __forceinline__ void pp_attention(const Src& src, const bf16* __restr
         for (int e = 0; e < 4; ++e) ov[e] = (bf16)(st.oacc[j][4 * rq + e] * inv);
         *reinterpret_cast<bf16x4*>(orow + 32 * j + 8 * rq + 4 * hh) = ov;
       }
+    if constexpr (LSE) {
+      const float m = st.m_ref == -INFINITY ? 0.f : st.m_ref;
+      if (hh == 0) lse[src.q_row_in(my_q)] = 0.69314718055994531f * (m + __log2f(l_tot));
+    }
   }
 }
 
@@ -643,11 +670,55 @@ __global__ __launch_bounds__(PP_NT, 1) void cluster_attn_kernel(ClusterAttnArgs 
   pp_attention<D>(src, a.q + off, a.k + off, a.v + off, a.o + off, src.n, qt * PP_BM, a.scale);
 }
 
+// Dense attention that also writes every row's log-sum-exp.
+template <int D>
+__global__ __launch_bounds__(PP_NT, 1) void attn_lse_kernel(AttnArgs a, int32_t nqb) {
+  const int32_t item = xcd_item((int32_t)blockIdx.x, (int32_t)gridDim.x);
+  const int32_t bh = item / nqb;
+  const int32_t qb = item - bh * nqb;
+  const size_t off = (size_t)bh * (size_t)a.S * D;
+  BandSource src;
+  src.rmap.divF = a.divF;
+  src.rmap.F = a.F;
+  src.rmap.P = a.P;
+  src.rmap.tm = false;
+  src.S = a.S;
+  src.band.S = a.S;
+  src.band.dense = 1;
+  src.band.divG = a.divP;
+  src.band.G = a.P;
+  src.band.NG = a.F;
+  src.band.w = 0;
+  pp_attention<D, BandSource, true>(src, a.q + off, a.k + off, a.v + off, a.o + off, a.S, qb * PP_BM, a.scale,
+                                    a.lse + (size_t)bh * a.S);
+}
+
+// One workgroup per (head, 256-row query block): attention over the block's chosen key blocks.
+template <int D>
+__global__ __launch_bounds__(PP_NT, 1) void block_attn_kernel(BlockAttnArgs a) {
+  const int32_t item = xcd_item((int32_t)blockIdx.x, (int32_t)gridDim.x);
+  const int32_t bh = item / a.nqb;
+  const int32_t qb = item - bh * a.nqb;
+  BlockSource src;
+  src.S = a.S;
+  src.q0 = qb * PP_BM;
+  src.n = min(PP_BM, a.S - src.q0);
+  src.L = min(max(a.blen[item], 0), a.S);
+  if (src.L == 0) return;
+  src.bl = a.blist + (size_t)item * a.nkb;
+  const size_t off = (size_t)bh * (size_t)a.S * D;
+  pp_attention<D>(src, a.q + off, a.k + off, a.v + off, a.o + off, src.n, 0, a.scale);
+}
+
 // Explicit instantiations, so that the host pass emits every launch stub the launchers use.
 template __global__ void attn_fwd_kernel<128>(AttnArgs, int32_t);
 template __global__ void attn_fwd_kernel<64>(AttnArgs, int32_t);
 template __global__ void cluster_attn_kernel<128>(ClusterAttnArgs);
 template __global__ void cluster_attn_kernel<64>(ClusterAttnArgs);
+template __global__ void attn_lse_kernel<128>(AttnArgs, int32_t);
+template __global__ void attn_lse_kernel<64>(AttnArgs, int32_t);
+template __global__ void block_attn_kernel<128>(BlockAttnArgs);
+template __global__ void block_attn_kernel<64>(BlockAttnArgs);
 
 }  // namespace
 
@@ -678,6 +749,32 @@ hipError_t launch_cluster_attention(const ClusterAttnArgs& a, hipStream_t st) {
     cluster_attn_kernel<128><<<grid, PP_NT, 0, st>>>(a);
   } else if (a.D == 64) {
     cluster_attn_kernel<64><<<grid, PP_NT, 0, st>>>(a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_lse(const AttnArgs& a, hipStream_t st) {
+  const int32_t nqb = (a.S + PP_BM - 1) / PP_BM;
+  const dim3 grid((unsigned)((int64_t)nqb * a.BH));
+  if (a.D == 128) {
+    attn_lse_kernel<128><<<grid, PP_NT, 0, st>>>(a, nqb);
+  } else if (a.D == 64) {
+    attn_lse_kernel<64><<<grid, PP_NT, 0, st>>>(a, nqb);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_block_attention(const BlockAttnArgs& a, hipStream_t st) {
+  static_assert(BLOCK_Q_ROWS == PP_BM && BLOCK_K_ROWS == BN, "search blocks are the attention kernel's tiles");
+  const dim3 grid((unsigned)((int64_t)a.nqb * a.BH));
+  if (a.D == 128) {
+    block_attn_kernel<128><<<grid, PP_NT, 0, st>>>(a);
+  } else if (a.D == 64) {
+    block_attn_kernel<64><<<grid, PP_NT, 0, st>>>(a);
   } else {
     return hipErrorInvalidValue;
   }

@@ -1,0 +1,270 @@
+// Head-adaptive block-sparse attention with an LSE-cached block search, after the AdaSpa
+// abstract ("Training-free and Adaptive Sparse Attention for Efficient Long Video Generation",
+// arXiv 2502.21079): the attention map is sparse in blocks; the log-sum-exp (LSE) of each query
+// row changes little across denoising steps, so an LSE cached from an earlier full-attention
+// step turns one pass of Q K^T into the exact attention mass of every block; each head then
+// keeps, per query block, the fewest key blocks that carry a given share of that mass.
+//
+//   block_mass_kernel    M[i][j] = sum over rows q of query block i (256 rows) and keys k of key
+//                        block j (64 keys) of exp(scale q.k - LSE_q): bf16 products on the
+//                        matrix cores, fp32 exponentials and sums.
+//   block_select_kernel  per (head, query block): key blocks in decreasing mass, the shortest
+//                        prefix reaching `coverage` of the row's total mass (fp64 prefix sums).
+//   block_lists_kernel   the chosen blocks of each query block in increasing order, and how
+//                        many keys they hold, for the attention kernel's gathered key tiles.
+#include "svg_internal.h"
+
+namespace svg {
+
+namespace {
+
+constexpr int BM_NT = 512;                 // 8 wavefronts x 32 query rows = one query block
+constexpr int BM_KT = BLOCK_K_ROWS;        // keys per tile = one key block
+
+// 8 wavefronts of 32 rows each hold the query block as MFMA B operands; key tiles of 64 rows are
+// the A operand from LDS (double-buffered in registers -> LDS, chunks XOR-swizzled by row).  The
+// accumulator S^T[key][query] gives lane l query l%32 and 16 keys per 32-key half; each lane
+// sums its 32 weights, the wavefront reduces over its lanes, and one thread adds the eight
+// wavefronts' sums in a fixed order, one tile behind.
+template <int D>
+__global__ __launch_bounds__(BM_NT) void block_mass_kernel(BlockMassArgs a) {
+  constexpr int NKS = D / 16;
+  constexpr int CPR = D / 8;
+  constexpr int RPB = 16 / CPR;
+  constexpr int PER_T = BM_KT * CPR / BM_NT;      // 16-byte chunks per thread per tile
+  static_assert(PER_T >= 1, "tile too small for the workgroup");
+  __shared__ __attribute__((aligned(16))) bf16 kt[2][BM_KT * D];
+  __shared__ float part[2][BM_NT / 64];
+
+  const int32_t bh = blockIdx.x / a.nqb;
+  const int32_t qb = blockIdx.x - bh * a.nqb;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int32_t S = a.S;
+  const int32_t row = qb * BLOCK_Q_ROWS + wave * 32 + l32;
+  const bf16* qh = a.q + (size_t)bh * S * D;
+  const bf16* kh = a.k + (size_t)bh * S * D;
+  bf16x8 qf[NKS];
+  const bf16* qr = qh + (size_t)min(row, S - 1) * D;
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qr + 16 * s + 8 * hh);
+  const float c = a.scale * 1.44269504088896340736f;
+  // rows past the sequence end weigh nothing
+  const float l2 = row < S ? a.lse[(size_t)bh * S + row] * 1.44269504088896340736f : INFINITY;
+  float* out = a.mass + (size_t)blockIdx.x * a.nkb;
+
+  u32x4 pre[PER_T];
+  auto fetch = [&](int32_t t) {
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const int o = tid + BM_NT * i;
+      const int32_t kr = min(t * BM_KT + o / CPR, S - 1);
+      pre[i] = *reinterpret_cast<const u32x4*>(kh + (size_t)kr * D + 8 * (o % CPR));
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const int o = tid + BM_NT * i;
+      const int r = o / CPR, q = o % CPR;
+      *reinterpret_cast<u32x4*>(&kt[buf][r * D + 8 * (q ^ ((r / RPB) & (CPR - 1)))]) = pre[i];
+    }
+  };
+  const int32_t nt = a.nkb;
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  for (int32_t t = 0; t < nt; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < nt) fetch(t + 1);
+    if (tid == 0 && t > 0) {
+      const float* pp = part[buf ^ 1];
+      float s = 0.f;
+#pragma unroll
+      for (int w = 0; w < BM_NT / 64; ++w) s += pp[w];
+      out[t - 1] = s;
+    }
+    f32x16 acc[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[blk][r] = 0.f;
+#pragma unroll
+    for (int s = 0; s < NKS; ++s)
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        const int r = blk * 32 + l32;
+        const bf16x8 ka =
+            *reinterpret_cast<const bf16x8*>(&kt[buf][r * D + 8 * ((2 * s + hh) ^ ((r / RPB) & (CPR - 1)))]);
+        acc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], acc[blk], 0, 0, 0);
+      }
+    float sum0 = 0.f, sum1 = 0.f;
+    const int32_t kend = S - t * BM_KT;      // keys of this tile that exist
+    if (kend >= BM_KT) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sum0 += __builtin_amdgcn_exp2f(fmaf(acc[0][r], c, -l2));
+        sum1 += __builtin_amdgcn_exp2f(fmaf(acc[1][r], c, -l2));
+      }
+    } else {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = blk * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+          const float p = __builtin_amdgcn_exp2f(fmaf(acc[blk][r], c, -l2));
+          if (key < kend) {
+            if (blk == 0) sum0 += p; else sum1 += p;
+          }
+        }
+    }
+    float s = sum0 + sum1;
+    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+    if (lane == 0) part[buf][wave] = s;
+    if (t + 1 < nt) stash(buf ^ 1);
+    __syncthreads();
+  }
+  if (tid == 0) {
+    const float* pp = part[(nt - 1) & 1];
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < BM_NT / 64; ++w) s += pp[w];
+    out[nt - 1] = s;
+  }
+}
+
+// Per (head, query block): bitonic sort of (mass, block) in LDS, decreasing mass and increasing
+// block among equal masses; fp64 prefix sums of the sorted masses; the shortest prefix that
+// reaches coverage * total (blocks of zero mass are never chosen).
+constexpr int SEL_NT = 512;
+__global__ __launch_bounds__(SEL_NT) void block_select_kernel(BlockSelectArgs a) {
+  __shared__ float w[BLOCK_MAX_NKB];
+  __shared__ int32_t ix[BLOCK_MAX_NKB];
+  __shared__ double part[SEL_NT];
+  __shared__ int32_t cut;
+  const int tid = threadIdx.x;
+  const int32_t nkb = a.nkb;
+  const float* m = a.mass + (size_t)blockIdx.x * nkb;
+  int n2 = 1;
+  while (n2 < nkb) n2 <<= 1;
+  for (int j = tid; j < n2; j += SEL_NT) {
+    w[j] = j < nkb ? m[j] : -1.f;
+    ix[j] = j;
+  }
+  if (tid == 0) cut = BLOCK_MAX_NKB;          // none yet
+  __syncthreads();
+  for (int k = 2; k <= n2; k <<= 1)
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      for (int x = tid; x < n2; x += SEL_NT) {
+        const int y = x ^ jj;
+        if (y > x) {
+          const bool up = (x & k) == 0;
+          const float wx = w[x], wy = w[y];
+          const int32_t ixx = ix[x], ixy = ix[y];
+          const bool x_first = wx > wy || (wx == wy && ixx < ixy);
+          if (x_first != up) {
+            w[x] = wy; w[y] = wx;
+            ix[x] = ixy; ix[y] = ixx;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  // thread tid owns sorted positions [tid * per, (tid + 1) * per)
+  const int per = (nkb + SEL_NT - 1) / SEL_NT;
+  const int lo = min(tid * per, nkb), hi = min(lo + per, nkb);
+  double own = 0.0;
+  for (int r = lo; r < hi; ++r) own += w[r] > 0.f ? (double)w[r] : 0.0;
+  part[tid] = own;
+  __syncthreads();
+  for (int o = 1; o < SEL_NT; o <<= 1) {
+    const double v = tid >= o ? part[tid - o] : 0.0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  const double total = part[SEL_NT - 1];
+  const double target = a.coverage * total;
+  double run = part[tid] - own;
+  for (int r = lo; r < hi; ++r) {
+    if (!(w[r] > 0.f)) break;
+    run += (double)w[r];
+    if (run >= target) {
+      atomicMin(&cut, r);
+      break;
+    }
+  }
+  __syncthreads();
+  // no prefix reaches the target (rounding with coverage 1): every block of positive mass
+  int32_t last = cut;
+  if (last >= nkb) {
+    last = -1;
+    for (int r = 0; r < nkb; ++r)
+      if (w[r] > 0.f) last = r;
+  }
+  uint8_t* srow = a.sel + (size_t)blockIdx.x * nkb;
+  for (int j = tid; j < nkb; j += SEL_NT) srow[j] = 0;
+  __syncthreads();
+  for (int r = tid; r <= last; r += SEL_NT) srow[ix[r]] = 1;
+}
+
+// Per (head, query block): the chosen key blocks in increasing order, and the keys they hold
+// (the sequence's last block may be partial; being the highest, it is last in the list).
+constexpr int BL_NT = 256;
+__global__ __launch_bounds__(BL_NT) void block_lists_kernel(BlockAttnArgs a) {
+  __shared__ int32_t part[BL_NT];
+  const int tid = threadIdx.x;
+  const int32_t nkb = a.nkb;
+  const uint8_t* srow = a.sel + (size_t)blockIdx.x * nkb;
+  int32_t* out = a.blist + (size_t)blockIdx.x * nkb;
+  const int per = (nkb + BL_NT - 1) / BL_NT;
+  const int lo = min(tid * per, nkb), hi = min(lo + per, nkb);
+  int32_t own = 0;
+  for (int j = lo; j < hi; ++j) own += srow[j] ? 1 : 0;
+  part[tid] = own;
+  __syncthreads();
+  for (int o = 1; o < BL_NT; o <<= 1) {
+    const int32_t v = tid >= o ? part[tid - o] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int32_t pos = part[tid] - own;
+  for (int j = lo; j < hi; ++j)
+    if (srow[j]) out[pos++] = j;
+  if (tid == 0) {
+    const int32_t n = part[BL_NT - 1];
+    int32_t keys = n * BLOCK_K_ROWS;
+    if (n > 0 && srow[nkb - 1]) keys -= nkb * BLOCK_K_ROWS - a.S;
+    a.blen[blockIdx.x] = keys;
+  }
+}
+
+// Explicit instantiations, so that the host pass emits every launch stub the launchers use.
+template __global__ void block_mass_kernel<128>(BlockMassArgs);
+template __global__ void block_mass_kernel<64>(BlockMassArgs);
+
+}  // namespace
+
+hipError_t launch_block_mass(const BlockMassArgs& a, hipStream_t st) {
+  const dim3 grid((unsigned)((int64_t)a.BH * a.nqb));
+  if (a.D == 128)
+    block_mass_kernel<128><<<grid, BM_NT, 0, st>>>(a);
+  else if (a.D == 64)
+    block_mass_kernel<64><<<grid, BM_NT, 0, st>>>(a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_block_select(const BlockSelectArgs& a, hipStream_t st) {
+  block_select_kernel<<<(unsigned)((int64_t)a.BH * a.nqb), SEL_NT, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_lists(const BlockAttnArgs& a, hipStream_t st) {
+  block_lists_kernel<<<(unsigned)((int64_t)a.BH * a.nqb), BL_NT, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace svg

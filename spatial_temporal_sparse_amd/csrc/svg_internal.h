@@ -125,8 +125,10 @@ struct AttnArgs {
   float scale;
   int32_t force_dense;
   int32_t fused_t;            // temporal heads read q/k/v and write o through the permutation
+  float* lse;                 // [BH][S] log-sum-exp of each row (launch_attention_lse only)
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
+hipError_t launch_attention_lse(const AttnArgs& a, hipStream_t st);   // dense, with lse
 
 struct ProfileArgs {
   const bf16 *q, *k, *v;
@@ -204,6 +206,42 @@ struct ClusterAttnArgs {
   float scale;
 };
 hipError_t launch_cluster_attention(const ClusterAttnArgs& a, hipStream_t st);
+
+// ------------------------------------------------------------------------------------------
+// Block-sparse path with an LSE-cached block search
+// ------------------------------------------------------------------------------------------
+constexpr int BLOCK_Q_ROWS = 256;   // query rows of a search block (an attention workgroup)
+constexpr int BLOCK_K_ROWS = 64;    // keys of a search block (an attention key tile)
+constexpr int BLOCK_MAX_NKB = 4096; // key blocks per row that the selection sorts in LDS
+
+struct BlockMassArgs {
+  const bf16 *q, *k;
+  const float* lse;           // [BH][S]
+  float* mass;                // [BH][nqb][nkb]
+  int32_t BH, S, D, nqb, nkb;
+  float scale;
+};
+hipError_t launch_block_mass(const BlockMassArgs& a, hipStream_t st);
+
+struct BlockSelectArgs {
+  const float* mass;          // [BH][nqb][nkb]
+  uint8_t* sel;               // [BH][nqb][nkb]
+  int32_t BH, nqb, nkb;
+  double coverage;
+};
+hipError_t launch_block_select(const BlockSelectArgs& a, hipStream_t st);
+
+struct BlockAttnArgs {
+  const bf16 *q, *k, *v;
+  bf16* o;
+  const uint8_t* sel;         // [BH][nqb][nkb]
+  int32_t* blist;             // workspace [BH][nqb][nkb]: chosen key blocks, increasing
+  int32_t* blen;              // workspace [BH][nqb]: keys of those blocks
+  int32_t BH, S, D, nqb, nkb;
+  float scale;
+};
+hipError_t launch_block_lists(const BlockAttnArgs& a, hipStream_t st);
+hipError_t launch_block_attention(const BlockAttnArgs& a, hipStream_t st);
 
 constexpr int ATTN_BM = 128;
 constexpr int ATTN_BN = 64;

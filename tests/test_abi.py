@@ -31,7 +31,8 @@ def test_header_declares_the_path():
     for n in ("svg_qknorm_rope", "svg_profile_heads", "svg_permute", "svg_unpermute", "svg_build_block_mask",
               "svg_sparse_attn", "svg_dense_attn", "svg_layer", "svg_dense_step", "svg_workspace_bytes",
               "svg_tile_shape", "svg_status_string", "svg_last_error", "svg_kmeans", "svg_centroid_topp",
-              "svg_cluster_attn"):
+              "svg_cluster_attn", "svg_dense_attn_lse", "svg_block_mass", "svg_block_select",
+              "svg_block_sparse_attn"):
         assert n in names
 
 
@@ -197,3 +198,23 @@ def test_clustering_argument_checks(svg):
                               None) == -4
     assert L.svg_cluster_attn(FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, good, 8, 16, 0.125, F2, FAKE, big_ws,
                               None) == -1
+
+
+def test_block_path_workspace_and_checks(svg):
+    L = svg.lib
+    g = svg.Geom(1, 24, 33, 45, 80, 128)
+    nqb, nkb = svg.block_grid(118800)
+    assert (nqb, nkb) == (465, 1857)
+    assert svg.workspace_bytes(svg.OP_BLOCK_ATTN, g) == -(-(24 * nqb * nkb * 4) // 256) * 256 + -(-(24 * nqb * 4) // 256) * 256
+    # more than 4096 key blocks
+    big = svg.Geom(1, 1, 8, 256, 129, 64)
+    assert svg.workspace_bytes(svg.OP_BLOCK_ATTN, big) == 0
+    small = svg.Geom(1, 2, 4, 8, 8, 64)
+    F2 = ctypes.c_void_p(0x200000)
+    assert L.svg_block_mass(FAKE, FAKE, FAKE, big, 0.125, F2, None) == -2
+    assert L.svg_block_mass(FAKE, FAKE, None, small, 0.125, F2, None) == -1
+    assert L.svg_block_select(FAKE, small, 0.0, F2, None) == -1
+    assert L.svg_block_select(FAKE, small, 1.5, F2, None) == -1
+    assert L.svg_block_sparse_attn(FAKE, FAKE, FAKE, FAKE, small, 0.125, F2, None, 0, None) == -4
+    assert L.svg_block_sparse_attn(FAKE, FAKE, FAKE, FAKE, small, 0.0, F2, FAKE, 1 << 20, None) == -1
+    assert L.svg_dense_attn_lse(FAKE, FAKE, FAKE, small, 0.125, F2, None, None) == -1
