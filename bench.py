@@ -32,6 +32,7 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_hunyuan720p_traffic.json")
 CLUSTER_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "cluster_attn_hunyuan720p_svg2_traffic.json")
+BLOCK_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "block_attn_hunyuan720p_blocks_traffic.json")
 
 
 def log(msg):
@@ -48,11 +49,13 @@ def parse():
                     help="layout transformation of temporal heads inside the attention kernel, or as separate "
                          "permute / unpermute passes")
     ap.add_argument("--no-compare", action="store_true", help="do not also time the other layout")
-    ap.add_argument("--workload", choices=("hunyuan720p_step", "cogvideox", "wan", "hunyuan720p_svg2"),
+    ap.add_argument("--workload", choices=("hunyuan720p_step", "cogvideox", "wan", "hunyuan720p_svg2",
+                                           "hunyuan720p_blocks"),
                     default="hunyuan720p_step",
                     help="token grid of the step (default: the HunyuanVideo-720p layer the headline is quoted on; "
                          "cogvideox and wan are the CogVideoX-like D=64 and the Wan-like grids; hunyuan720p_svg2 "
-                         "times the semantic clustering path instead, on the 720p grid)")
+                         "times the semantic clustering path instead, on the 720p grid; hunyuan720p_blocks the head-adaptive "
+                         "block-sparse path with an LSE-cached search)")
     ap.add_argument("--denoise", type=int, default=0, metavar="N",
                     help="instead: time the attention layers of an N-step denoising loop through the step driver "
                          "(dense attention for the first quarter of the steps, then profiling + sparse attention), "
@@ -380,6 +383,168 @@ def cluster_bench(args):
     print(json.dumps(result), flush=True)
 
 
+def block_cpu_baseline(q, k, v, sel, D):
+    """The fp64 oracle's attention over the chosen blocks for 4096 sampled query rows of one head
+    (given the GPU's choice); token-level FLOPs / wall time."""
+    import numpy as np
+    import oracle.adaspa_oracle as A
+    try:
+        import threadpoolctl
+        threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    f64 = lambda t: t.detach().cpu().double().numpy()
+    S = q.shape[2]
+    rows = np.sort(np.random.default_rng(321).choice(S, 4096, replace=False))
+    s = sel[0, 0].cpu().numpy().astype(bool)
+    qh, kh, vh = f64(q[0, 0]), f64(k[0, 0]), f64(v[0, 0])
+    t0 = time.perf_counter()
+    A.block_sparse_attention_rows(qh, kh, vh, s, rows, 1.0 / math.sqrt(D))
+    el = time.perf_counter() - t0
+    pairs = float(A.block_token_mask(s, rows, S).sum())
+    return {"value": 4.0 * D * pairs / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 numpy oracle, attention over the chosen blocks of 4096 sampled query rows of one head "
+                      f"(S={S}, D={D}) given the GPU's block choice; token-level FLOPs",
+            "seconds": round(el, 2)}
+
+
+def block_bench(args):
+    """The head-adaptive block-sparse path at the 720p grid.  Per layer, a dense step (attention
+    with each row's log-sum-exp, cached) precedes the timed sparse step on the next step's
+    activations: block search with the cached LSE, block choice, attention over the chosen
+    blocks.  Also timed: a sparse step that reuses the previous step's block choice."""
+    import numpy as np
+    import torch
+
+    import spatial_temporal_sparse_amd as svg
+    from workloads import WORKLOADS, make_qkv
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = WORKLOADS["hunyuan720p"]
+    g = wl.geom
+    F, HH, WW, D = g.F, g.HH, g.WW, g.D
+    S, BH = g.S, g.B * g.H
+    cov = 0.9
+    L = max(1, min(args.layers, 2))
+    nqb, nkb = svg.block_grid(S)
+    log(f"[bench] block path: {L} layers of {g}, blocks {svg.BLOCK_Q}x{svg.BLOCK_K}, coverage {cov}")
+    layers = []
+    for l in range(L):
+        q0, k0, v0 = make_qkv(wl, device="cuda", layer=l, step=0)
+        _, lse = svg.dense_attn_lse(q0, k0, v0, F, HH, WW)        # the dense step: LSE cached
+        del q0, k0, v0
+        q, k, v = make_qkv(wl, device="cuda", layer=l, step=1)
+        bufs = {"lse": lse, "mass": torch.empty((g.B, g.H, nqb, nkb), dtype=torch.float32, device=dev),
+                "sel": torch.empty((g.B, g.H, nqb, nkb), dtype=torch.uint8, device=dev), "o": torch.empty_like(q),
+                "ws": torch.empty(max(256, svg.workspace_bytes(svg.OP_BLOCK_ATTN, svg.geometry(q, F, HH, WW))),
+                                  dtype=torch.uint8, device=dev)}
+        layers.append((q, k, v, bufs))
+    torch.cuda.synchronize()
+
+    def step(l, ev=None, search=True):
+        q, k, v, b = layers[l]
+        if ev is not None:
+            ev[0].record()
+        if search:
+            svg.block_mass(q, k, b["lse"], F, HH, WW, mass=b["mass"])
+        if ev is not None:
+            ev[1].record()
+        if search:
+            svg.block_select(b["mass"], F, HH, WW, D, cov, sel=b["sel"])
+        if ev is not None:
+            ev[2].record()
+        svg.block_sparse_attn(q, k, v, b["sel"], F, HH, WW, o=b["o"], ws=b["ws"])
+        if ev is not None:
+            ev[3].record()
+
+    def timed(search):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(i % L, evs[i], search)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        st = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(3)] for i in range(args.steps)])
+        return ms, st
+
+    for i in range(max(args.warmup, L)):
+        step(i % L)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done; timing {args.steps} steps with the search, then {args.steps} reusing the choice")
+    ms_search, st = timed(True)
+    ms_reuse, st_reuse = timed(False)
+    names = ["block_mass", "block_select", "block_sparse_attn"]
+    stage_ms = {n: float(st[:, j].mean()) for j, n in enumerate(names)}
+    # work of the chosen blocks: each query block runs its rows against its chosen keys
+    fl_tok, fl_tile, dens = [], [], []
+    for (q, k, v, b) in layers:
+        sel = b["sel"].double()
+        kb = torch.full((nkb,), float(svg.BLOCK_K), dtype=torch.float64, device=dev)
+        kb[-1] = S - svg.BLOCK_K * (nkb - 1)
+        qrows = torch.full((nqb,), float(svg.BLOCK_Q), dtype=torch.float64, device=dev)
+        qrows[-1] = S - svg.BLOCK_Q * (nqb - 1)
+        keys = torch.einsum("bhij,j->bhi", sel, kb)                      # keys per query block
+        fl_tok.append(4.0 * D * float(torch.einsum("bhi,i->", keys, qrows)))
+        fl_tile.append(4.0 * D * float((torch.ceil(keys / 64) * 64).sum()) * svg.BLOCK_Q)
+        dens.append(float(torch.einsum("bhi,i->bh", keys, qrows).mean()) / S ** 2)
+    tok = np.array([fl_tok[i % L] for i in range(args.steps)])
+    tile = np.array([fl_tile[i % L] for i in range(args.steps)])
+    attn_tflops = float(np.mean(tile / (st[:, 2] * 1e-3)) / 1e12)
+    q, k, v, b = layers[0]
+    od = torch.empty_like(q)
+    svg.dense_attn(q, k, v, F, HH, WW, o=od)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    svg.dense_attn(q, k, v, F, HH, WW, o=od)
+    e1.record()
+    torch.cuda.synchronize()
+    dense_ms = e0.elapsed_time(e1)
+    e0.record()
+    svg.dense_attn_lse(q, k, v, F, HH, WW, o=od, lse=torch.empty_like(b["lse"]))
+    e1.record()
+    torch.cuda.synchronize()
+    dense_lse_ms = e0.elapsed_time(e1)
+    mass_flops = 2.0 * D * S * S * BH
+    log(f"[bench] {ms_search:.3f} ms/step with search, {ms_reuse:.3f} reusing; stages "
+        f"{json.dumps({k_: round(v_, 4) for k_, v_ in stage_ms.items()})}")
+    result = {
+        "metric": "block-sparse attn ms/layer + effective TFLOP/s (% bf16 MFMA peak), 720p shape, LSE-cached block "
+                  "search",
+        "value": round(float(np.mean(tok)) / (ms_search * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_search, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"hunyuan720p (planted spatial/temporal heads): per layer, the block search of step 1 "
+                               f"with the LSE cached by a dense step 0, block choice at coverage {cov}, attention "
+                               f"over the chosen blocks, over {L} layers",
+                   "B": g.B, "H": g.H, "F": F, "HH": HH, "WW": WW, "S": S, "D": D, "block": [svg.BLOCK_Q, svg.BLOCK_K],
+                   "coverage": cov, "layers": L, "parallelism": "single GPU"},
+        "density": round(float(np.mean(dens)), 4),
+        "token_tflop_per_layer": round(float(tok.mean()) / 1e12, 4),
+        "tile_tflop_per_layer": round(float(tile.mean()) / 1e12, 4),
+        "block_sparse_attn_ms": round(stage_ms["block_sparse_attn"], 4),
+        "block_sparse_attn_tflops_tile": round(attn_tflops, 2),
+        "block_mass_ms": round(stage_ms["block_mass"], 4),
+        "block_mass_tflops": round(mass_flops / (stage_ms["block_mass"] * 1e-3) / 1e12, 2),
+        "block_select_ms": round(stage_ms["block_select"], 4),
+        "ms_per_step_reusing_choice": round(ms_reuse, 4),
+        "dense_attn_ms": round(dense_ms, 3),
+        "dense_attn_lse_ms": round(dense_lse_ms, 3),
+        "speedup_vs_dense_step": round(dense_ms / ms_search, 3),
+        "speedup_vs_dense_step_reusing_choice": round(dense_ms / ms_reuse, 3),
+        "stage_ms": {k_: round(v_, 4) for k_, v_ in stage_ms.items()},
+        "roofline": {"bound": "mfma", "kernel": f"block_attn_kernel<{D}>", "achieved": round(attn_tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(BLOCK_TRAFFIC_FILE),
+                     "note": "computed-tile FLOPs over the svg_block_sparse_attn call (block lists + attention kernel)"},
+    }
+    log("[bench] timing the CPU oracle on a bounded sample")
+    result["cpu_baseline"] = block_cpu_baseline(q, k, v, b["sel"], D)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -397,6 +562,9 @@ def main():
         sys.exit(2)
     if args.workload == "hunyuan720p_svg2":
         cluster_bench(args)
+        return
+    if args.workload == "hunyuan720p_blocks":
+        block_bench(args)
         return
     import numpy as np
     import torch

@@ -7,7 +7,8 @@
 //
 //   block_mass_kernel    M[i][j] = sum over rows q of query block i (256 rows) and keys k of key
 //                        block j (64 keys) of exp(scale q.k - LSE_q): bf16 products on the
-//                        matrix cores, fp32 exponentials and sums.
+//                        matrix cores, fp32 exponentials and sums; a wavefront skips the
+//                        exponentials of a tile in which all its weights are below 2^-40.
 //   block_select_kernel  per (head, query block): key blocks in decreasing mass, the shortest
 //                        prefix reaching `coverage` of the row's total mass (fp64 prefix sums).
 //   block_lists_kernel   the chosen blocks of each query block in increasing order, and how
@@ -100,23 +101,33 @@ __global__ __launch_bounds__(BM_NT) void block_mass_kernel(BlockMassArgs a) {
       }
     float sum0 = 0.f, sum1 = 0.f;
     const int32_t kend = S - t * BM_KT;      // keys of this tile that exist
-    if (kend >= BM_KT) {
+    // a tile whose largest weight for every query of the wavefront is below 2^-40 is skipped:
+    // that moves a block's mass by less than 2^-26 (16384 weights), far below its fp32 rounding
+    // at the row totals the choice compares against
+    float mx = acc[0][0];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sum0 += __builtin_amdgcn_exp2f(fmaf(acc[0][r], c, -l2));
-        sum1 += __builtin_amdgcn_exp2f(fmaf(acc[1][r], c, -l2));
-      }
-    } else {
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, acc[0][r]);
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[1][r]);
+    if (__any(fmaf(mx, c, -l2) > -40.f)) {
+      if (kend >= BM_KT) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = blk * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-          const float p = __builtin_amdgcn_exp2f(fmaf(acc[blk][r], c, -l2));
-          if (key < kend) {
-            if (blk == 0) sum0 += p; else sum1 += p;
-          }
+          sum0 += __builtin_amdgcn_exp2f(fmaf(acc[0][r], c, -l2));
+          sum1 += __builtin_amdgcn_exp2f(fmaf(acc[1][r], c, -l2));
         }
+      } else {
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = blk * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+            const float p = __builtin_amdgcn_exp2f(fmaf(acc[blk][r], c, -l2));
+            if (key < kend) {
+              if (blk == 0) sum0 += p; else sum1 += p;
+            }
+          }
+      }
     }
     float s = sum0 + sum1;
     for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);

@@ -119,13 +119,15 @@ def _plant(x: torch.Tensor, geom: Geometry, kinds: np.ndarray, u_sp: torch.Tenso
             xv[:, h] += scale * u_tp[h].view(1, 1, P, D)
 
 
-def make_qkv(wl: Workload, device: str = "cpu", layer: int = 0, dtype=torch.bfloat16):
+def make_qkv(wl: Workload, device: str = "cpu", layer: int = 0, dtype=torch.bfloat16, step: int = 0):
     """Q, K, V as [B, H, S, D] tensors of `dtype` (bf16 by default; RNE from fp32).
 
     Values are drawn in fp32 with a seeded generator on `device` and cast once.
     On "cpu" the draw is bit-reproducible everywhere; on a GPU it is
     reproducible for a given device type.  `layer` offsets the seed so that
-    each layer of a multi-layer step gets fresh activations.
+    each layer of a multi-layer step gets fresh activations.  `step` > 0 redraws
+    the N(0, 1) part (a later denoising step of the same layer) and keeps the
+    planted per-head vectors and kinds.
     """
     g = wl.geom
     gen = torch.Generator(device=device)
@@ -138,6 +140,12 @@ def make_qkv(wl: Workload, device: str = "cpu", layer: int = 0, dtype=torch.bflo
         kinds = planted_kinds(g.H, wl.seed * 1000 + layer)
         u_sp = torch.randn((g.H, g.F, g.D), generator=gen, device=device, dtype=torch.float32)
         u_tp = torch.randn((g.H, g.P, g.D), generator=gen, device=device, dtype=torch.float32)
+    if step > 0:
+        gen.manual_seed((wl.seed * 1000 + layer) * 7919 + step)
+        q.normal_(generator=gen)
+        k.normal_(generator=gen)
+        v.normal_(generator=gen)
+    if wl.planted:
         _plant(q, g, kinds, u_sp, u_tp, wl.plant_scale)
         _plant(k, g, kinds, u_sp, u_tp, wl.plant_scale)
         del u_sp, u_tp
