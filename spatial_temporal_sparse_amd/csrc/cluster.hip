@@ -512,19 +512,36 @@ __global__ __launch_bounds__(KL_NT) void cluster_keylist_kernel(const uint8_t* _
 }
 
 // Work items of the attention kernel: (query cluster << 16) | 256-row tile, per head, in cluster
-// order; unused slots -1.
-__global__ void cluster_items_kernel(const int32_t* __restrict__ q_off, int32_t* __restrict__ items, int32_t Cq,
-                                     int32_t per_head, int32_t tile_rows) {
+// order; unused slots -1.  One workgroup per head: thread c counts cluster c's tiles, a block scan
+// places them.
+constexpr int IT_NT = 1024;
+__global__ __launch_bounds__(IT_NT) void cluster_items_kernel(const int32_t* __restrict__ q_off,
+                                                             int32_t* __restrict__ items, int32_t Cq,
+                                                             int32_t per_head, int32_t tile_rows) {
+  __shared__ int32_t part[IT_NT];
   const int32_t bh = blockIdx.x;
-  if (threadIdx.x != 0) return;
+  const int tid = threadIdx.x;
   const int32_t* off = q_off + (size_t)bh * (Cq + 1);
   int32_t* it = items + (size_t)bh * per_head;
-  int32_t n = 0;
-  for (int32_t c = 0; c < Cq; ++c) {
-    const int32_t rows = off[c + 1] - off[c];
-    for (int32_t t = 0; t * tile_rows < rows && n < per_head; ++t) it[n++] = (c << 16) | t;
+  int32_t carry = 0;
+  for (int32_t c0 = 0; c0 < Cq; c0 += IT_NT) {
+    const int32_t c = c0 + tid;
+    const int32_t rows = c < Cq ? max(off[c + 1] - off[c], 0) : 0;
+    const int32_t nt = (rows + tile_rows - 1) / tile_rows;
+    __syncthreads();
+    part[tid] = nt;
+    __syncthreads();
+    for (int o = 1; o < IT_NT; o <<= 1) {
+      const int32_t v = tid >= o ? part[tid - o] : 0;
+      __syncthreads();
+      part[tid] += v;
+      __syncthreads();
+    }
+    const int32_t first = carry + part[tid] - nt;
+    for (int32_t t = 0; t < nt && first + t < per_head; ++t) it[first + t] = (c << 16) | t;
+    carry += part[IT_NT - 1];
   }
-  for (; n < per_head; ++n) it[n] = -1;
+  for (int32_t n = carry + tid; n < per_head; n += IT_NT) it[n] = -1;
 }
 
 // Explicit instantiations, so that the host pass emits every launch stub the launchers use.
@@ -579,7 +596,7 @@ hipError_t launch_centroid_topp(const ToppArgs& a, hipStream_t st) {
 hipError_t launch_cluster_lists(const ClusterListArgs& a, hipStream_t st) {
   const dim3 g((unsigned)a.Cq, (unsigned)a.BH);
   cluster_keylist_kernel<<<g, KL_NT, 0, st>>>(a.sel, a.k_perm, a.k_off, a.klist, a.klen, a.S, a.Cq, a.Ck);
-  cluster_items_kernel<<<(unsigned)a.BH, 64, 0, st>>>(a.q_off, a.items, a.Cq, a.items_per_head, a.tile_rows);
+  cluster_items_kernel<<<(unsigned)a.BH, IT_NT, 0, st>>>(a.q_off, a.items, a.Cq, a.items_per_head, a.tile_rows);
   return hipGetLastError();
 }
 
