@@ -47,7 +47,7 @@ extern "C" {
 typedef int32_t svg_status;
 #define SVG_OK               0
 #define SVG_ERR_INVALID     (-1)   /* a null pointer, bad size, bad window, misaligned pointer ... */
-#define SVG_ERR_UNSUPPORTED (-2)   /* a valid request this build does not implement (e.g. D not in {64,128}) */
+#define SVG_ERR_UNSUPPORTED (-2)   /* a valid request the library does not implement (e.g. D not in {64,128}) */
 #define SVG_ERR_HIP         (-3)   /* the HIP runtime reported an error while enqueueing */
 #define SVG_ERR_WORKSPACE   (-4)   /* ws is NULL or smaller than svg_workspace_bytes() */
 

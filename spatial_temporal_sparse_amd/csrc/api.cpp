@@ -692,7 +692,7 @@ SVG_API const char* svg_status_string(svg_status s) {
   switch (s) {
     case SVG_OK: return "SVG_OK: success";
     case SVG_ERR_INVALID: return "SVG_ERR_INVALID: invalid argument";
-    case SVG_ERR_UNSUPPORTED: return "SVG_ERR_UNSUPPORTED: request not supported by this build";
+    case SVG_ERR_UNSUPPORTED: return "SVG_ERR_UNSUPPORTED: request not supported by the library";
     case SVG_ERR_HIP: return "SVG_ERR_HIP: HIP runtime error";
     case SVG_ERR_WORKSPACE: return "SVG_ERR_WORKSPACE: workspace missing or too small";
     default: return "unknown svg_status";
