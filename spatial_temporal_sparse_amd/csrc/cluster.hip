@@ -66,9 +66,10 @@ __global__ void kmeans_init_kernel(const bf16* __restrict__ x, const int32_t* __
 // current one is multiplied.  The accumulator starts at -|c|^2/2 of its centroid, so it ends at
 // the score x.c - |c|^2/2 itself.  It gives each lane one row and 16 centroids per 32-block in
 // increasing order: a lane takes the tile's maximum, and only when that beats its best so far
-// looks up which centroid gave it (the first one, the lowest index among equals).
+// looks up which centroid gave it (the first one, the lowest index among equals).  Four
+// workgroups fit a CU (at most 128 VGPRs), so that one's loads overlap the others' products.
 template <int D>
-__global__ __launch_bounds__(AS_NT) void kmeans_assign_kernel(const bf16* __restrict__ x, const bf16* __restrict__ cb,
+__global__ __launch_bounds__(AS_NT, 4) void kmeans_assign_kernel(const bf16* __restrict__ x, const bf16* __restrict__ cb,
                                                               const float* __restrict__ hn, int32_t* __restrict__ labels,
                                                               int32_t S, int32_t Cpad, int32_t nrb) {
   constexpr int NKS = D / 16;
