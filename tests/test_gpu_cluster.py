@@ -303,3 +303,38 @@ def test_one_token_per_cluster(gpu):
         _check_topp(w, s, wl.p, f"h{h}")
         want = O2.semantic_attention(qh[0, h], kh[0, h], vh[0, h], lq, lk, s.astype(bool), sc)
         assert_close_attn(oh[0, h], want, f"h{h}")
+
+
+def test_more_than_1024_clusters(gpu):
+    """Cluster counts past one scan block (C > 1024): the counting sort's and the work items'
+    multi-pass scans, and attention over 1100 query clusters."""
+    g = Geometry(1, 1, 4, 24, 24, 64)                     # S = 2304
+    wl = _semantic("many_clusters", g, 6, 1100, 1000, 0.9, 2, 37)
+    note("C = 2000 / 1100 / 1000 clusters")
+    q, k, v, iq, ik = _inputs(wl)
+    i2000 = torch.from_numpy(init_token_indices(g.S, 2000, 38)).to(DEV)
+    big = gpu.kmeans(q, g.F, g.HH, g.WW, 2000, 1, init_idx=i2000)
+    cq = gpu.kmeans(q, g.F, g.HH, g.WW, wl.Cq, 2, init_idx=iq)
+    ck = gpu.kmeans(k, g.F, g.HH, g.WW, wl.Ck, 2, init_idx=ik)
+    sel = gpu.centroid_topp(cq, ck, g.F, g.HH, g.WW, wl.p)
+    o = gpu.cluster_attn(q, k, v, cq, ck, sel, g.F, g.HH, g.WW)
+    torch.cuda.synchronize()
+    qh, kh, vh = host64(q)[0, 0], host64(k)[0, 0], host64(v)[0, 0]
+    rng = np.random.default_rng(3)
+    rows = np.sort(rng.choice(g.S, 256, replace=False))
+    lab = big.labels[0, 0].cpu().numpy().astype(np.int64)
+    _check_sort(lab, big.perm[0, 0].cpu().numpy(), big.offsets[0, 0].cpu().numpy(), 2000, "C=2000")
+    cent0 = O2.init_centroids(qh, i2000.cpu().numpy())
+    _check_assignment(qh[rows], cent0, lab[rows], "C=2000 assignment")
+    _check_update(qh, lab, cent0, big.centroids[0, 0].cpu().numpy(), "C=2000 means")
+    for cl, C, x, tag in ((cq, wl.Cq, qh, "Q"), (ck, wl.Ck, kh, "K")):
+        l = cl.labels[0, 0].cpu().numpy().astype(np.int64)
+        _check_sort(l, cl.perm[0, 0].cpu().numpy(), cl.offsets[0, 0].cpu().numpy(), C, tag)
+    s = sel[0, 0].cpu().numpy()
+    sc = 1.0 / np.sqrt(g.D)
+    w = O2.centroid_weights(cq.centroids[0, 0].cpu().numpy(), ck.centroids[0, 0].cpu().numpy(),
+                            np.diff(ck.offsets[0, 0].cpu().numpy()), sc)
+    _check_topp(w, s, wl.p, "top-p")
+    want = O2.semantic_attention_rows(qh, kh, vh, rows, cq.labels[0, 0].cpu().numpy(), ck.labels[0, 0].cpu().numpy(),
+                                      s.astype(bool), sc)
+    assert_close_attn(host64(o[0, 0])[rows], want, "1100 query clusters")
