@@ -88,6 +88,37 @@ def test_scale_argument(gpu):
         assert_close_attn(oh[0, h], want, f"scale 0.3 h{h}")
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["explicit", "fused"])
+def test_sharp_softmax(gpu, fused):
+    """Planted inputs at scale 1.0 (logits spanning hundreds): the running max moves by more
+    than the lazy-rescale slack many times along a row, and most weights underflow; the keys
+    are also presented with the row's largest score late (keys in reverse order of a ramp)."""
+    g = Geometry(1, 3, 4, 10, 12, 128)
+    note(f"sharp softmax fused={fused}")
+    q, k, v = _inputs("sharp", g, True, seed=24)
+    # a ramp along the keys: later keys get larger scores for every query of head 2
+    ramp = torch.linspace(0.0, 6.0, g.S, device=DEV).view(1, 1, g.S, 1)
+    k = (k.float() + ramp * torch.ones_like(k.float()) * (torch.arange(g.H, device=DEV) == 2).view(1, g.H, 1, 1))
+    k = k.to(torch.bfloat16)
+    q = (q.float().abs() * ((torch.arange(g.H, device=DEV) == 2).view(1, g.H, 1, 1)) + q.float() *
+         ((torch.arange(g.H, device=DEV) != 2).view(1, g.H, 1, 1))).to(torch.bfloat16)
+    kinds = np.array([[O.SPATIAL, O.TEMPORAL, O.DENSE]], dtype=np.uint8)
+    kd = torch.from_numpy(kinds).to(DEV)
+    if fused:
+        o, _ = gpu.sparse_attn(q, k, v, None, None, None, kd, g.F, g.HH, g.WW, 1, 3, scale=1.0)
+    else:
+        qt, kt, vt = (gpu.permute(t, g.F, g.HH, g.WW, kd) for t in (q, k, v))
+        o, ot = gpu.sparse_attn(q, k, v, qt, kt, vt, kd, g.F, g.HH, g.WW, 1, 3, scale=1.0)
+        gpu.unpermute(ot, g.F, g.HH, g.WW, kd, out=o)
+    torch.cuda.synchronize()
+    qh, kh, vh, oh = host64(q), host64(k), host64(v), host64(o)
+    for h in range(g.H):
+        logits = qh[0, h] @ kh[0, h].T
+        assert logits.max() - logits.min() > 100.0        # the case is as sharp as intended
+        want = O.head_attention(qh[0, h], kh[0, h], vh[0, h], int(kinds[0, h]), g.F, g.P, 1, 3, 1.0)
+        assert_close_attn(oh[0, h], want, f"sharp h{h}")
+
+
 def test_all_dense_kinds_equal_dense_kernel_bitwise(gpu):
     g = Geometry(1, 4, 5, 10, 13, 128)
     note("all-dense kinds vs dense kernel")
