@@ -33,6 +33,7 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_hunyuan720p_traffic.json")
 CLUSTER_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "cluster_attn_hunyuan720p_svg2_traffic.json")
 BLOCK_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "block_attn_hunyuan720p_blocks_traffic.json")
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_busy_hunyuan720p.json")
 
 
 def log(msg):
@@ -123,6 +124,21 @@ def measured_traffic(path=TRAFFIC_FILE):
     if t.get("kernel_sha") != kernel_sha():
         return None
     return t.get("bytes_per_launch")
+
+
+def measured_mfma(kernel):
+    """MFMA busy fraction and clock of an attention kernel at 720p from the committed counter
+    runs (SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE), if they were taken on the current kernel
+    source; else an empty dict."""
+    try:
+        with open(MFMA_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return {}
+    k = t.get("kernels", {}).get(kernel)
+    if t.get("kernel_sha") != kernel_sha() or k is None:
+        return {}
+    return {"mfma_busy": round(k["mfma_busy"], 3), "clock_ghz": round(k["clock_ghz"], 2)}
 
 
 def cpu_baseline(q, k, v, kinds, g, w_f, w_p):
@@ -376,6 +392,7 @@ def cluster_bench(args):
         "roofline": {"bound": "mfma", "kernel": f"cluster_attn_kernel<{D}>", "achieved": round(attn_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(CLUSTER_TRAFFIC_FILE),
+                     **measured_mfma("cluster_attn_kernel<128>, 720p clustering layer"),
                      "note": "computed-tile FLOPs over the svg_cluster_attn call (key lists + attention kernel)"},
     }
     log("[bench] timing the CPU oracle on a bounded sample")
@@ -538,6 +555,7 @@ def block_bench(args):
         "roofline": {"bound": "mfma", "kernel": f"block_attn_kernel<{D}>", "achieved": round(attn_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(BLOCK_TRAFFIC_FILE),
+                     **measured_mfma("block_attn_kernel<128>, 720p block-sparse layer"),
                      "note": "computed-tile FLOPs over the svg_block_sparse_attn call (block lists + attention kernel)"},
     }
     log("[bench] timing the CPU oracle on a bounded sample")
@@ -726,7 +744,8 @@ def main():
         "hbm_frac_of_peak": {k: round(v / PEAK_HBM_GBS, 3) for k, v in hbm.items()},
         "roofline": {"bound": "mfma", "kernel": f"attn_fwd_kernel<{D}>", "achieved": round(attn_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic},
+                     "traffic": traffic,
+                     **(measured_mfma("attn_fwd_kernel<128>, sparse 720p layer") if headline else {})},
     }
     log("[bench] timing the CPU oracle on a bounded sample")
     qn = bufs.qn  # the last layer's normalised Q/K; pair them with that layer's V
