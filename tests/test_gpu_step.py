@@ -77,3 +77,19 @@ def test_step_wan_shape_with_norm(gpu):
     wl = WORKLOADS["wan"]
     note(f"full layer {wl.name} {wl.geom}")
     _check_layer(gpu, wl, rows_per_head=32, heads=range(0, wl.geom.H, 5))
+
+
+def test_step_cogvideox_shape(gpu):
+    """The CogVideoX-like grid (48 heads, 13 x 30 x 45 tokens, D = 64): profiling choices and
+    sampled output rows of every sixth head."""
+    wl = WORKLOADS["cogvideox"]
+    note(f"full layer {wl.name} {wl.geom}")
+    _check_layer(gpu, wl, rows_per_head=32, heads=range(0, wl.geom.H, 6))
+
+
+@pytest.mark.parametrize("layer", [1, 2, 3])
+def test_step_720p_subgrid_later_layers(gpu, layer):
+    """Layers 1-3 of the four-layer step on fresh inputs (4-frame sub-grid of the 720p layer)."""
+    wl = WORKLOADS["hunyuan720p_f4"]
+    note(f"full layer {wl.name} layer {layer}")
+    _check_layer(gpu, wl, rows_per_head=48, heads=range(layer, wl.geom.H, 4), layer=layer, planted_expected=False)
