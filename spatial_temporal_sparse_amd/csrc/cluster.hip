@@ -462,10 +462,12 @@ __global__ __launch_bounds__(KL_NT) void cluster_keylist_kernel(const uint8_t* _
   // thread tid owns clusters [tid * per, ...): selected count and key count
   const int per = (Ck + KL_NT - 1) / KL_NT;
   const int c_lo = min(tid * per, Ck), c_hi = min(c_lo + per, Ck);
+  // A cluster's size comes from the caller's offsets; it is clamped to [0, S], and every key
+  // count below saturates at S, so a list never outgrows its S-entry row whatever the offsets.
+  auto csize = [&](int c) { return min(max(off[c + 1] - off[c], 0), S); };
   int32_t nsel = 0, nkey = 0;
   for (int c = c_lo; c < c_hi; ++c)
-    if (srow[c]) { ++nsel; nkey += off[c + 1] - off[c]; }
-  // scan of (nsel, nkey) packed: nkey < 2^31 / ... kept separate for clarity
+    if (srow[c]) { ++nsel; nkey = min(nkey + csize(c), S); }
   part[tid] = nsel;
   __syncthreads();
   for (int o = 1; o < KL_NT; o <<= 1) {
@@ -479,20 +481,21 @@ __global__ __launch_bounds__(KL_NT) void cluster_keylist_kernel(const uint8_t* _
   __syncthreads();
   part[tid] = nkey;
   __syncthreads();
+  // inclusive scan with saturating addition (associative on non-negative counts)
   for (int o = 1; o < KL_NT; o <<= 1) {
     const int32_t v = tid >= o ? part[tid - o] : 0;
     __syncthreads();
-    part[tid] += v;
+    part[tid] = min(part[tid] + v, S);
     __syncthreads();
   }
-  int32_t pos = part[tid] - nkey;
+  int32_t pos = tid > 0 ? part[tid - 1] : 0;
   const int32_t L = part[KL_NT - 1];
   for (int c = c_lo; c < c_hi; ++c)
     if (srow[c]) {
       start[m] = pos;
       cid[m] = c;
       ++m;
-      pos += off[c + 1] - off[c];
+      pos = min(pos + csize(c), S);
     }
   if (tid == 0) {
     start[msel] = L;

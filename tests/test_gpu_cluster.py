@@ -338,3 +338,43 @@ def test_more_than_1024_clusters(gpu):
     want = O2.semantic_attention_rows(qh, kh, vh, rows, cq.labels[0, 0].cpu().numpy(), ck.labels[0, 0].cpu().numpy(),
                                       s.astype(bool), sc)
     assert_close_attn(host64(o[0, 0])[rows], want, "1100 query clusters")
+
+
+def test_inconsistent_key_offsets_stay_in_bounds(gpu):
+    """Key offsets that are non-monotone, negative or far beyond S: every key list is clamped
+    to S entries of in-range rows, so the call writes nothing outside its buffers and every
+    output row is a finite mean of V rows."""
+    svg = gpu
+    g = Geometry(1, 2, 3, 5, 7, 64)
+    S = g.S
+    note(f"cluster attention with inconsistent key offsets, S={S}")
+    gen = torch.Generator(device="cpu").manual_seed(77)
+    q, k, v = (torch.randn((g.B, g.H, S, g.D), generator=gen).to(torch.bfloat16).to(DEV) for _ in range(3))
+    Cq, Ck = 3, 5
+    q_off = torch.tensor([0, 40, 70, S], dtype=torch.int32).repeat(g.B, g.H, 1).contiguous()
+    # non-monotone, negative and oversized key offsets
+    k_off = torch.tensor([0, S, 3, 4 * S, -5, 2 * S], dtype=torch.int32).repeat(g.B, g.H, 1).contiguous()
+    perm = torch.arange(S, dtype=torch.int32).repeat(g.B, g.H, 1).contiguous()
+    cq = svg.Clusters(torch.zeros((g.B, g.H, Cq, g.D)), torch.zeros_like(perm), perm, q_off)
+    ck = svg.Clusters(torch.zeros((g.B, g.H, Ck, g.D)), torch.zeros_like(perm), perm, k_off)
+    cq = svg.Clusters(*(t.to(DEV) for t in (cq.centroids, cq.labels, cq.perm, cq.offsets)))
+    ck = svg.Clusters(*(t.to(DEV) for t in (ck.centroids, ck.labels, ck.perm, ck.offsets)))
+    sel = torch.ones((g.B, g.H, Cq, Ck), dtype=torch.uint8, device=DEV)
+    nbytes = svg.workspace_bytes(svg.OP_CLUSTER_ATTN, svg.geometry(q, g.F, g.HH, g.WW), Cq)
+    # a guard region after the workspace must stay untouched
+    guard = 1 << 16
+    ws = torch.full((nbytes + guard,), 0xA5, dtype=torch.uint8, device=DEV)
+    o = svg.cluster_attn(q, k, v, cq, ck, sel, g.F, g.HH, g.WW, ws=ws[:nbytes])
+    torch.cuda.synchronize()
+    BH = g.B * g.H
+    align = lambda n: (n + 255) // 256 * 256
+    klen_off = align(BH * Cq * S * 4)
+    klen = ws[klen_off:klen_off + BH * Cq * 4].view(torch.int32).cpu().numpy()
+    assert (klen >= 0).all() and (klen <= S).all(), klen
+    assert (ws[nbytes:].cpu().numpy() == 0xA5).all(), "write past the workspace"
+    klist = ws[:BH * Cq * S * 4].view(torch.int32).cpu().numpy().reshape(BH, Cq, S)
+    for bh in range(BH):
+        for c in range(Cq):
+            rows = klist[bh, c, :klen[bh * Cq + c]]
+            assert ((rows >= 0) & (rows < S)).all()
+    assert torch.isfinite(o.float()).all()

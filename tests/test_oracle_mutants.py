@@ -107,7 +107,37 @@ def _mut_block_mask_layout(kind, F, P, w_f, w_p, bm, bn, q_blocks=None):
     return out
 
 
-ORIG = {n: getattr(O, n) for n in ("attention", "profile_head", "rms_norm", "rope_3d", "block_mask")}
+def _mut_qknorm_swap_weights(q, k, wq, wk, eps, F, HH, WW, base, dims=None):
+    return ORIG["qknorm_rope"](q, k, wk, wq, eps, F, HH, WW, base, dims)                  # weights exchanged
+
+
+def _mut_qknorm_rope_first(q, k, wq, wk, eps, F, HH, WW, base, dims=None):
+    return (O.rms_norm(O.rope_3d(q, F, HH, WW, base, dims), wq, eps),                   # RoPE before the norm
+            O.rms_norm(O.rope_3d(k, F, HH, WW, base, dims), wk, eps))
+
+
+def _mut_qknorm_q_only(q, k, wq, wk, eps, F, HH, WW, base, dims=None):
+    qo, _ = ORIG["qknorm_rope"](q, k, wq, wk, eps, F, HH, WW, base, dims)
+    return qo, O.rope_3d(k, F, HH, WW, base, dims)                                     # K not normalised
+
+
+def _mut_agree_always(kind_a, kind_b, mse_ref, rel_tie=1e-6):
+    return np.ones(np.shape(kind_a), dtype=bool)                                       # vacuous checker
+
+
+def _mut_agree_min_ref(kind_a, kind_b, mse_ref, rel_tie=1e-6):
+    a, c = mse_ref[..., 0], mse_ref[..., 1]
+    near = np.abs(a - c) <= rel_tie * np.maximum(np.minimum(a, c), 1e-300)             # gap relative to the smaller
+    return (kind_a == kind_b) | near
+
+
+def _mut_agree_absolute(kind_a, kind_b, mse_ref, rel_tie=1e-6):
+    a, c = mse_ref[..., 0], mse_ref[..., 1]
+    return (kind_a == kind_b) | (np.abs(a - c) <= rel_tie)                             # absolute, not relative
+
+
+ORIG = {n: getattr(O, n) for n in ("attention", "profile_head", "rms_norm", "rope_3d", "block_mask",
+                                  "qknorm_rope", "choices_agree")}
 
 MUTANTS = [
     ("mask_spatial", _mut_spatial_strict),
@@ -127,6 +157,12 @@ MUTANTS = [
     ("rope_3d", _mut_rope_axes),
     ("block_mask", _mut_block_mask_floor),
     ("block_mask", _mut_block_mask_layout),
+    ("qknorm_rope", _mut_qknorm_swap_weights),
+    ("qknorm_rope", _mut_qknorm_rope_first),
+    ("qknorm_rope", _mut_qknorm_q_only),
+    ("choices_agree", _mut_agree_always),
+    ("choices_agree", _mut_agree_min_ref),
+    ("choices_agree", _mut_agree_absolute),
 ]
 
 

@@ -420,6 +420,85 @@ def pin_rope_complex_form():
     assert np.abs(got - want).max() < 1e-12
 
 
+def _norm_rope_row_loop(row, w, eps, f, yy, xx, D, base):
+    """One token row through RMSNorm then 3D RoPE, written as plain scalar loops.
+
+    The slice widths and pairing are restated here from the readings (frame slice
+    D - 4*floor(D/6), row and column slices 2*floor(D/6) each; interleaved pairs),
+    not taken from the oracle.
+    """
+    ss = 0.0
+    for c in range(D):
+        ss += float(row[c]) * float(row[c])
+    inv = 1.0 / math.sqrt(ss / D + eps)
+    y = [float(row[c]) * inv * float(w[c]) for c in range(D)]
+    third = 2 * (D // 6)
+    out = list(y)
+    off = 0
+    for width, pos in ((D - 2 * third, f), (third, yy), (third, xx)):
+        for j in range(width // 2):
+            th = pos * base ** (-2.0 * j / width)
+            a, b = y[off + 2 * j], y[off + 2 * j + 1]
+            out[off + 2 * j] = a * math.cos(th) - b * math.sin(th)
+            out[off + 2 * j + 1] = a * math.sin(th) + b * math.cos(th)
+        off += width
+    return out
+
+
+def pin_qknorm_rope_row_loop():
+    """QK-Norm then RoPE, Q with its own weight and K with its own, against scalar loops.
+
+    The weights differ inside every rotated pair, so rotating before normalising
+    (or exchanging the two weight vectors) changes the result.
+    """
+    F, HH, WW, D = 3, 2, 4, 24
+    P, S = HH * WW, F * HH * WW
+    r = _rng(15)
+    q = r.standard_normal((1, 2, S, D)) * 2.5
+    k = r.standard_normal((1, 2, S, D)) * 0.7
+    wq = r.uniform(0.5, 1.5, D)
+    wk = r.uniform(0.5, 1.5, D)
+    eps = 1e-6
+    gq, gk = O.qknorm_rope(q, k, wq, wk, eps, F, HH, WW, 10000.0)
+    for h in range(2):
+        for t in range(S):
+            f, rem = divmod(t, P)
+            yy, xx = divmod(rem, WW)
+            wantq = _norm_rope_row_loop(q[0, h, t], wq, eps, f, yy, xx, D, 10000.0)
+            wantk = _norm_rope_row_loop(k[0, h, t], wk, eps, f, yy, xx, D, 10000.0)
+            assert np.abs(gq[0, h, t] - wantq).max() < 1e-12, (h, t)
+            assert np.abs(gk[0, h, t] - wantk).max() < 1e-12, (h, t)
+
+
+# ----------------------------------------------------------------------------- choice checker
+def pin_choices_agree_hand_cases():
+    """The head-choice comparison: equal kinds agree; different kinds agree only inside
+    a relative gap of 1e-6 of the larger reference error."""
+    sp, tp = O.SPATIAL, O.TEMPORAL
+    kinds = lambda *v: np.array(v, dtype=np.uint8)
+    # equal choices agree whatever the errors
+    assert O.choices_agree(kinds(sp, tp), kinds(sp, tp), np.array([[1.0, 2.0], [3.0, 0.5]])).all()
+    # a clear disagreement (10% apart) is reported
+    got = O.choices_agree(kinds(sp, tp), kinds(tp, tp), np.array([[1.0, 1.1], [3.0, 0.5]]))
+    assert got.tolist() == [False, True]
+    # 5e-7 relative apart: a near tie, either choice accepted
+    assert O.choices_agree(kinds(tp), kinds(sp), np.array([[1.0, 1.0 + 5e-7]])).all()
+    # 2e-6 relative apart: not a tie
+    assert not O.choices_agree(kinds(tp), kinds(sp), np.array([[1.0, 1.0 + 2e-6]])).any()
+    # the gap is relative to the LARGER error: d = 1.0000005e-6 is within 1e-6 of 1 + d
+    # but not within 1e-6 of 1
+    d = 1.0000005e-6
+    assert O.choices_agree(kinds(tp), kinds(sp), np.array([[1.0, 1.0 + d]])).all()
+    assert O.choices_agree(kinds(sp), kinds(tp), np.array([[1.0 + d, 1.0]])).all()
+    # the relative rule scales: errors of 1e-20 and 1.1e-20 are 10% apart
+    assert not O.choices_agree(kinds(sp), kinds(tp), np.array([[1e-20, 1.1e-20]])).any()
+    # both errors zero: an exact tie
+    assert O.choices_agree(kinds(sp), kinds(tp), np.array([[0.0, 0.0]])).all()
+    # shapes [B, H] are kept
+    out = O.choices_agree(np.zeros((2, 3), np.uint8), np.ones((2, 3), np.uint8), np.ones((2, 3, 2)))
+    assert out.shape == (2, 3) and out.all()
+
+
 # -------------------------------------------------------------------------------------- step
 def pin_full_step_consistency():
     from workloads import Geometry, Workload, make_qkv, bf16_to_f64, norm_weights
