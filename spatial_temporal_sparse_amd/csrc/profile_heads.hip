@@ -18,16 +18,21 @@
 //                                 permuted identically on both operands).
 // The three states share one running reference max, the unmasked one: softmax does not
 // depend on the reference, so each masked state only selects the unmasked exponentials of
-// its keys.  This is exact up to rounding while a row's masked scores stay within 126 (log2
-// units) of its unmasked maximum; beyond that the masked exponentials underflow.
+// its keys.  This is exact up to rounding while a row's masked scores stay within about 126
+// (log2 units) of the split's unmasked maximum; beyond that the masked exponentials
+// underflow.  A masked state whose row sum in a split falls below 2^-100 although the split
+// holds keys of its mask is therefore marked (row sum -1) instead of stored, and pass 2
+// recomputes that state of that row exactly, with its own maximum.
 // Keys are frame-major here: the spatial mask is a per-query interval of frames, the
 // temporal mask compares in-frame positions (key mod P).  Each wavefront writes the
 // unnormalised partial state (reference max, row sum, O) of its queries to the workspace.
 // Key and value tiles are copied HBM -> LDS (global_load_lds_dwordx4, no register staging)
 // into two buffers, one tile ahead of their use.
 // Pass 2: one workgroup per (head, sampled row) merges that row's partial states with
-// log-sum-exp weights, forms its three outputs (one channel per thread) and sums the two
-// squared errors over the channels in fp64.
+// log-sum-exp weights taken against each state's own largest log-mass (so that no split's
+// weight underflows against another state's maximum), forms its three outputs (one channel
+// per thread; a marked state by the exact fallback) and sums the two squared errors over the
+// channels in fp64.
 // Pass 3: one workgroup per head sums the per-row errors in a fixed order, stores mse (fp32)
 // and the kind, deciding on the stored fp32 values (ties -> spatial).
 // HBM-bound: K and V of every head are read once.
@@ -47,6 +52,9 @@ constexpr int QG = 64;             // sampled queries per workgroup
 constexpr int MAX_SPLIT = 128;
 constexpr int TARGET_WGS = 512;    // two workgroups per CU
 constexpr float RESCALE_SLACK = 8.0f;
+// A masked state's row sum in a split below this (relative to the split's unmasked reference)
+// may have lost keys to underflow; such a state is recomputed exactly.
+constexpr float UNDERFLOW_GUARD = 0x1p-100f;
 
 // s_waitcnt immediate (gfx9 encoding): at most vm vector-memory loads and lgkm LDS operations
 // outstanding, exports not waited for.
@@ -334,12 +342,26 @@ __global__ __launch_bounds__(NT, 2) void profile_partial_kernel(ProfileArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(VMCNT0);
 
+  // ---- does this split hold keys of each mask for this lane's query? ----
+  bool has_keys[3];
+  has_keys[0] = true;
+  has_keys[1] = max(sp_lo, ks) < min(sp_hi, ke);
+  {
+    const int32_t plo = max(0, pq - a.w_p), phi = min(a.P - 1, pq + a.w_p);
+    const int32_t f0 = (int32_t)fdiv((uint32_t)ks, a.divP), f1 = (int32_t)fdiv((uint32_t)(ke - 1), a.divP);
+    bool any = f1 - f0 >= 2;
+    any = any || (f0 * a.P + phi >= ks && f0 * a.P + plo <= ke - 1);
+    any = any || (f1 > f0 && f1 * a.P + plo <= ke - 1);
+    has_keys[2] = any;
+  }
+
   // ---- this wavefront's partial states: row sums over the four lane groups ----
   const int32_t qpad = a.n_zq * QG;
   const int32_t qloc = zq * QG + wave * 16 + i16;
 #pragma unroll
   for (int x = 0; x < 3; ++x) {
-    const float l_tot = sum_x32(sum_x16(st.l[x]));
+    float l_tot = sum_x32(sum_x16(st.l[x]));
+    if (x > 0 && has_keys[x] && !(l_tot >= UNDERFLOW_GUARD)) l_tot = -1.f;   // mark for the exact fallback
     const size_t slot = (((size_t)bh * a.nsplit + split) * 3 + x) * qpad + qloc;
     if (g == 0) {
       a.part_ml[slot * 2 + 0] = st.m_ref;
@@ -359,10 +381,83 @@ template __global__ void profile_partial_kernel<128, TP_INTERVAL>(ProfileArgs);
 template __global__ void profile_partial_kernel<64, TP_PER_KEY>(ProfileArgs);
 template __global__ void profile_partial_kernel<64, TP_INTERVAL>(ProfileArgs);
 
+// Exact attention output (channel tid) of sampled row tq under mask x (1 spatial, 2 temporal),
+// with the state's own maximum and fp32 weights: the fallback for a state whose exponentials
+// underflowed against the shared reference.  All D threads of the workgroup take part.
+template <int D>
+__device__ float exact_masked_row(const ProfileArgs& a, int32_t bh, int32_t tq, int x, float* qs, float* wb,
+                                  float* red) {
+  const int tid = threadIdx.x;
+  const size_t off = (size_t)bh * (size_t)a.S * D;
+  const bf16* K = a.k + off;
+  const bf16* V = a.v + off;
+  const int32_t fq = (int32_t)fdiv((uint32_t)tq, a.divP);
+  const int32_t pq = tq - fq * a.P;
+  int32_t n_keys, base, wlen;
+  if (x == 1) {
+    base = max(0, fq - a.w_f) * a.P;
+    n_keys = min(a.F, fq + a.w_f + 1) * a.P - base;
+    wlen = n_keys;
+  } else {
+    base = max(0, pq - a.w_p);
+    wlen = min(a.P - 1, pq + a.w_p) - base + 1;
+    n_keys = a.F * wlen;
+  }
+  auto key = [&](int32_t n) { return x == 1 ? base + n : (n / wlen) * a.P + base + n % wlen; };
+  auto score = [&](int32_t t) {
+    const bf16* kr = K + (size_t)t * D;
+    float s = 0.f;
+#pragma unroll 4
+    for (int c8 = 0; c8 < D; c8 += 8) {
+      const bf16x8 kv = *reinterpret_cast<const bf16x8*>(kr + c8);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s = fmaf(qs[c8 + j], (float)kv[j], s);
+    }
+    return s;
+  };
+  qs[tid] = (float)a.q[off + (size_t)tq * D + tid];
+  __syncthreads();
+  // maximum of the state's scores
+  float m = -INFINITY;
+  for (int32_t n = tid; n < n_keys; n += D) m = fmaxf(m, score(key(n)));
+  red[tid] = m;
+  __syncthreads();
+  for (int s2 = D / 2; s2 > 0; s2 >>= 1) {
+    if (tid < s2) red[tid] = fmaxf(red[tid], red[tid + s2]);
+    __syncthreads();
+  }
+  const float M = red[0];
+  __syncthreads();
+  const float c = a.scale * 1.44269504088896340736f;
+  // weights D keys at a time; thread tid then accumulates channel tid over them
+  float o = 0.f, l = 0.f;
+  for (int32_t n0 = 0; n0 < n_keys; n0 += D) {
+    const int32_t n = n0 + tid;
+    const float w = n < n_keys ? exp2f((score(key(n)) - M) * c) : 0.f;
+    wb[tid] = w;
+    l += w;
+    __syncthreads();
+    const int32_t cnt = min(D, n_keys - n0);
+    for (int32_t j = 0; j < cnt; ++j) o = fmaf(wb[j], (float)V[(size_t)key(n0 + j) * D + tid], o);
+    __syncthreads();
+  }
+  red[tid] = l;
+  __syncthreads();
+  for (int s2 = D / 2; s2 > 0; s2 >>= 1) {
+    if (tid < s2) red[tid] += red[tid + s2];
+    __syncthreads();
+  }
+  const float L = red[0];
+  __syncthreads();
+  return o / L;
+}
+
 template <int D>
 __global__ __launch_bounds__(D) void profile_merge_kernel(ProfileArgs a) {
   __shared__ float sm[3][MAX_SPLIT], sl[3][MAX_SPLIT], wt[3][MAX_SPLIT];
+  __shared__ int marked[3];
   __shared__ double red[2][D];
+  __shared__ float fb_q[D], fb_w[D], fb_red[D];
   const int32_t bh = blockIdx.x / a.n_q;
   const int32_t qg = blockIdx.x - bh * a.n_q;
   const int tid = threadIdx.x;
@@ -376,21 +471,32 @@ __global__ __launch_bounds__(D) void profile_merge_kernel(ProfileArgs a) {
   }
   __syncthreads();
   if (tid < 3) {
+    // split p holds 2^(sm + log2 sl) of the state's mass; weights are taken against the largest
+    int mk = 0;
     float M = -INFINITY;
-    for (int32_t p = 0; p < nparts; ++p) M = fmaxf(M, sm[tid][p]);
+    for (int32_t p = 0; p < nparts; ++p) {
+      if (sl[tid][p] < 0.f) mk = 1;
+      if (sl[tid][p] > 0.f) M = fmaxf(M, sm[tid][p] + __log2f(sl[tid][p]));
+    }
     float L = 0.f;
     for (int32_t p = 0; p < nparts; ++p) {
-      const float w = (sm[tid][p] == -INFINITY) ? 0.f : exp2f(sm[tid][p] - M);
+      const float w = sl[tid][p] > 0.f ? exp2f(sm[tid][p] - M) : 0.f;
       wt[tid][p] = w;
       L += w * sl[tid][p];
     }
     const float inv = (L > 0.f) ? 1.f / L : 0.f;
     for (int32_t p = 0; p < nparts; ++p) wt[tid][p] *= inv;
+    marked[tid] = mk;
   }
   __syncthreads();
   float o3[3];
 #pragma unroll
   for (int x = 0; x < 3; ++x) {
+    if (marked[x]) {   // uniform across the workgroup
+      const int32_t tq = min(max(a.idx[qg], 0), a.S - 1);
+      o3[x] = exact_masked_row<D>(a, bh, tq, x, fb_q, fb_w, fb_red);
+      continue;
+    }
     float s = 0.f;
     for (int32_t p = 0; p < nparts; ++p) {
       const size_t slot = (((size_t)bh * nparts + p) * 3 + x) * qpad + qg;

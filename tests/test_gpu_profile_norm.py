@@ -135,3 +135,49 @@ def test_qknorm_rope_vs_oracle(gpu, case):
     q2, k2 = q.clone(), k.clone()
     gpu.qknorm_rope(q2, k2, tq, tk, g.F, g.HH, g.WW, 1e-6, 10000.0, dims, q_out=q2, k_out=k2)
     assert torch.equal(q2, qo) and torch.equal(k2, ko)
+
+
+# Sharp rows: a sampled query meets one planted key of huge score outside both of its masks,
+# so that its masked scores lie far more than 126 (log2 units) below its unmasked maximum.
+# The shared-reference fast path loses such a state's exponentials to underflow; the kernel
+# must then merge by each state's own mass and recompute the marked states exactly.
+SHARP_CASES = [  # name, F, HH, WW, D, w_p
+    ("P64_interval_D128", 8, 8, 8, 128, 3),
+    ("P48_per_key_D64", 10, 6, 8, 64, 3),
+]
+
+
+@pytest.mark.parametrize("case", SHARP_CASES, ids=[c[0] for c in SHARP_CASES])
+def test_profile_sharp_rows(gpu, case):
+    name, F, HH, WW, D, w_p = case
+    g = Geometry(1, 2, F, HH, WW, D)
+    note(f"profile sharp rows {name}")
+    q, k, v = make_qkv(Workload("sharp", g, 1, w_p, 64, 41, 141, planted=False), device="cpu")
+    idx = sample_queries(g.S, 64, 141)
+    P = g.P
+    c = O.default_scale(D) * np.log2(np.e)
+    qf, kf = q.float(), k.float()
+    planted = []
+    for h in range(g.H):
+        for j in (0, 7, 30):
+            tq = int(idx[j])
+            fq, pq = divmod(tq, P)
+            # a key outside both masks: at least two frames away and w_p + 2 positions away
+            ff = (fq + F // 2) % F
+            pf = (pq + P // 2) % P
+            assert abs(ff - fq) > 1 and abs(pf - pq) > w_p
+            t_far = ff * P + pf
+            qv = qf[0, h, tq]
+            kf[0, h, t_far] = qv * (170.0 / (c * float(qv.norm()) ** 2))   # score of about 170 log2 units
+            planted.append((h, tq))
+    k = kf.to(torch.bfloat16)
+    # the planted rows are in the regime: every masked score far below the unmasked maximum
+    q64, k64 = q.double().numpy(), k.double().numpy()
+    for h, tq in planted:
+        sc = (q64[0, h, tq] @ k64[0, h].T) * c
+        t = np.arange(g.S)
+        sp = np.abs(t // P - tq // P) <= 1
+        tp = np.abs(t % P - tq % P) <= w_p
+        assert sc.max() - sc[sp].max() > 140 and sc.max() - sc[tp].max() > 140
+    q, k, v = q.to(DEV), k.to(DEV), v.to(DEV)
+    _check_profile(gpu, q, k, v, idx, g, 1, w_p, what=name)

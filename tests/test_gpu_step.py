@@ -93,3 +93,61 @@ def test_step_720p_subgrid_later_layers(gpu, layer):
     wl = WORKLOADS["hunyuan720p_f4"]
     note(f"full layer {wl.name} layer {layer}")
     _check_layer(gpu, wl, rows_per_head=48, heads=range(layer, wl.geom.H, 4), layer=layer, planted_expected=False)
+
+
+# The benchmarked layer itself: the 720p grid with QK-RMSNorm + 3D RoPE over 33 frames, four
+# layers of fresh inputs, run through svg_layer (norm, profiling, block-sparse attention with
+# the fused layout transformation), on exactly the inputs the benchmark generates.
+BENCHED = [  # layer, heads, sampled output rows per head
+    (0, range(0, 12), 256),
+    (0, range(12, 24), 256),
+    (1, range(0, 24), 64),
+    (2, range(0, 24), 64),
+    (3, range(0, 24), 64),
+]
+
+
+@pytest.mark.parametrize("layer,heads,n_rows", BENCHED,
+                         ids=[f"layer{l}_heads{h.start}-{h.stop - 1}" for l, h, _ in BENCHED])
+def test_benched_720p_step_layer(gpu, layer, heads, n_rows):
+    wl = WORKLOADS["hunyuan720p_step"]
+    g = wl.geom
+    note(f"benched layer {wl.name} layer {layer} heads {heads.start}-{heads.stop - 1} {g}")
+    q, k, v = make_qkv(wl, device=DEV, layer=layer)
+    idx = sample_queries(g.S, wl.n_q, wl.idx_seed + layer)
+    wq, wk = norm_weights(g.D, wl.seed)
+    norm = (torch.from_numpy(wq).to(DEV), torch.from_numpy(wk).to(DEV), wl.eps, wl.rope_base)
+    o, kind, mse, qn, kn = gpu.layer(q, k, v, torch.from_numpy(idx).to(DEV), g.F, g.HH, g.WW, wl.w_f, wl.w_p,
+                                     norm=norm)
+    # the benchmark's own call sequence (separate stage calls, fused layout) gives the same bits
+    o2, kind2, _, _, _ = gpu.sparse_layer(q, k, v, torch.from_numpy(idx).to(DEV), g.F, g.HH, g.WW, wl.w_f, wl.w_p,
+                                          norm=norm, fused=True)
+    torch.cuda.synchronize()
+    assert torch.equal(kind2, kind) and torch.equal(o2, o)
+    del o2
+    kind, mse = kind.cpu().numpy(), mse.cpu().numpy()
+    sc = O.default_scale(g.D)
+    # norm + RoPE: every row of two heads, frames 0..32 of the rotation table
+    if layer == 0:
+        for h in list(heads)[:1] + list(heads)[-1:]:
+            for src, w, out in ((q, wq, qn), (k, wk, kn)):
+                want = O.rope_3d(O.rms_norm(host64(src[0, h]), w.astype(np.float64), wl.eps), g.F, g.HH, g.WW,
+                                 wl.rope_base)
+                pair = np.repeat(np.hypot(want[:, 0::2], want[:, 1::2]), 2, axis=1)
+                bad = np.abs(host64(out[0, h]) - want) > bf16_ulp(want) + 1e-6 + 2.0 ** -20 * pair
+                assert not bad.any(), f"norm/RoPE head {h}: {bad.sum()} elements off"
+    pi = O.perm_indices(g.F, g.P)
+    rng = np.random.default_rng(500 + layer)
+    ends = np.arange(256)
+    for h in heads:
+        qh, kh, vh = host64(qn[0, h]), host64(kn[0, h]), host64(v[0, h])
+        a, c, kd = O.profile_head(qh, kh, vh, idx, g.F, g.P, wl.w_f, wl.w_p, sc)
+        assert O.choices_agree(np.array([kind[0, h]]), np.array([kd]), np.array([[a, c]]), 1e-6).all(), \
+            (layer, h, kind[0, h], kd, a, c, mse[0, h])
+        # the first and last 256-row query block of the head's working layout, plus random rows
+        blocks = np.concatenate([ends, g.S - 256 + ends])
+        if kind[0, h] == O.TEMPORAL:
+            blocks = pi[blocks]
+        rows = np.unique(np.concatenate([rng.choice(g.S, n_rows, replace=False), blocks]))
+        want = O.head_attention_rows(qh, kh, vh, rows, int(kind[0, h]), g.F, g.P, wl.w_f, wl.w_p, sc)
+        assert_close_attn(host64(o[0, h])[rows], want, f"layer {layer} head {h} kind {kind[0, h]}")
