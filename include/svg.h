@@ -202,6 +202,26 @@ svg_status svg_layer(const void* q, const void* k, const void* v, const float* w
                      void* o, float* mse_out, uint8_t* kind_out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * svg_layer_noalloc -- svg_layer for callers that cannot allocate device memory or hand in a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, checks, kernels and results as svg_layer, without ws and
+ * ws_bytes: the scratch memory lives in a static device array of
+ * SVG_LAYER_NOALLOC_SCRATCH_BYTES, one copy per device, held until the process ends; its
+ * address is looked up once per device (with that device current) on the first call there.
+ * The call allocates nothing.
+ * Requests whose svg_workspace_bytes(SVG_OP_LAYER, &g, n_q) exceeds that size return
+ * SVG_ERR_WORKSPACE before anything is enqueued.  `stream` must belong to the current device
+ * (SVG_ERR_INVALID otherwise).  Every call on one device shares that device's scratch and
+ * leaves its contents behind: calls that may overlap on one device (different streams, or
+ * host threads) race and must be serialised by the caller.
+ */
+#define SVG_LAYER_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+svg_status svg_layer_noalloc(const void* q, const void* k, const void* v, const float* wq, const float* wk,
+                             float eps, float rope_base, int32_t dt, int32_t dh, int32_t dw, void* qn, void* kn,
+                             const int32_t* q_idx, int32_t n_q, svg_geom g, svg_windows w, float scale,
+                             int32_t dense, void* o, float* mse_out, uint8_t* kind_out, void* stream);
+
+/*
  * svg_dense_step -- the step schedule of [svg-authors] other optimisations: the first
  * dense_fraction of the n_steps denoising steps run dense attention, the rest sparse.
  * Step s (0-based) runs dense iff s < dense_fraction * n_steps, i.e. the first

@@ -28,6 +28,8 @@ OP_SPARSE_ATTN = 2
 OP_LAYER = 3
 OP_KMEANS = 4
 OP_CLUSTER_ATTN = 5
+# size of svg_layer_noalloc's static per-device scratch (SVG_LAYER_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 OP_BLOCK_ATTN = 6
 BLOCK_Q = 256
 BLOCK_K = 64
@@ -66,6 +68,9 @@ _SIGNATURES = {
     "svg_layer": (_st, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, ctypes.c_float, ctypes.c_float, _c_i32, _c_i32, _c_i32,
                        _c_vp, _c_vp, _c_vp, _c_i32, Geom, Windows, ctypes.c_float, _c_i32, _c_vp, _c_vp, _c_vp,
                        _c_vp, ctypes.c_size_t, _c_vp]),
+    "svg_layer_noalloc": (_st, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, ctypes.c_float, ctypes.c_float, _c_i32, _c_i32,
+                               _c_i32, _c_vp, _c_vp, _c_vp, _c_i32, Geom, Windows, ctypes.c_float, _c_i32, _c_vp,
+                               _c_vp, _c_vp, _c_vp]),
     "svg_dense_step": (_c_i32, [_c_i32, _c_i32, ctypes.c_float]),
     "svg_kmeans": (_st, [_c_vp, Geom, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, ctypes.c_size_t,
                         _c_vp]),
@@ -337,12 +342,9 @@ def dense_step(step: int, n_steps: int, dense_fraction: float = 0.25) -> bool:
     return r == 1
 
 
-def layer(q, k, v, q_idx, F, HH, WW, w_f, w_p, dense=False, norm=None, dims=None, scale=None, o=None, qn=None,
-          kn=None, mse=None, kind=None, ws=None):
-    """One attention layer in one library call (svg_layer): [QK-RMSNorm + 3D RoPE], then dense
-    attention (dense=True) or profiling + block-sparse attention with the fused layout
-    transformation.  norm: None or (wq, wk, eps, rope_base).  Returns (o, kind, mse, q', k'),
-    where q', k' are what attention read; kind and mse are not written by a dense layer."""
+def _layer_args(q, k, v, q_idx, F, HH, WW, w_f, w_p, dense, norm, dims, scale, o, qn, kn, mse, kind):
+    """Checked ctypes arguments of svg_layer / svg_layer_noalloc up to the workspace, and the
+    outputs (o, kind, mse, q', k') the call writes."""
     g = geometry(q, F, HH, WW)
     shp = _shape(g)
     dev = q.device
@@ -368,12 +370,35 @@ def layer(q, k, v, q_idx, F, HH, WW, w_f, w_p, dense=False, norm=None, dims=None
         _check_qkv("qn", qn, shp, device=dev)
         _check_qkv("kn", kn, shp, device=dev)
     dt, dh, dw = rope_split(g.D) if dims is None else dims
-    ws = _workspace(OP_LAYER, g, n_q, dev, ws)
     sc = default_scale(g.D) if scale is None else scale
-    _check(lib.svg_layer(_ptr(q), _ptr(k), _ptr(v), _ptr(wq), _ptr(wk), float(eps), float(base), dt, dh, dw,
-                         _ptr(qn), _ptr(kn), _ptr(q_idx), n_q, g, Windows(w_f, w_p), float(sc), int(bool(dense)),
-                         _ptr(o), _ptr(mse), _ptr(kind), _ptr(ws), ws.numel(), _stream(q)))
-    return o, kind, mse, (qn if norm is not None else q), (kn if norm is not None else k)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(wq), _ptr(wk), float(eps), float(base), dt, dh, dw, _ptr(qn), _ptr(kn),
+            _ptr(q_idx), n_q, g, Windows(w_f, w_p), float(sc), int(bool(dense)), _ptr(o), _ptr(mse), _ptr(kind))
+    outs = (o, kind, mse, (qn if norm is not None else q), (kn if norm is not None else k))
+    return g, n_q, args, outs
+
+
+def layer(q, k, v, q_idx, F, HH, WW, w_f, w_p, dense=False, norm=None, dims=None, scale=None, o=None, qn=None,
+          kn=None, mse=None, kind=None, ws=None):
+    """One attention layer in one library call (svg_layer): [QK-RMSNorm + 3D RoPE], then dense
+    attention (dense=True) or profiling + block-sparse attention with the fused layout
+    transformation.  norm: None or (wq, wk, eps, rope_base).  Returns (o, kind, mse, q', k'),
+    where q', k' are what attention read; kind and mse are not written by a dense layer."""
+    g, n_q, args, outs = _layer_args(q, k, v, q_idx, F, HH, WW, w_f, w_p, dense, norm, dims, scale, o, qn, kn, mse,
+                                     kind)
+    ws = _workspace(OP_LAYER, g, n_q, q.device, ws)
+    _check(lib.svg_layer(*args, _ptr(ws), ws.numel(), _stream(q)))
+    return outs
+
+
+def layer_noalloc(q, k, v, q_idx, F, HH, WW, w_f, w_p, dense=False, norm=None, dims=None, scale=None, o=None,
+                  qn=None, kn=None, mse=None, kind=None):
+    """layer() through svg_layer_noalloc: the library's static per-device scratch instead of a
+    workspace, so the call allocates nothing when every output buffer is passed in.  Calls
+    that overlap on one device share that scratch and must not run concurrently."""
+    _, _, args, outs = _layer_args(q, k, v, q_idx, F, HH, WW, w_f, w_p, dense, norm, dims, scale, o, qn, kn, mse,
+                                   kind)
+    _check(lib.svg_layer_noalloc(*args, _stream(q)))
+    return outs
 
 
 class StepDriver:

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/svg.h"
@@ -373,6 +374,68 @@ SVG_API svg_status svg_layer(const void* q, const void* k, const void* v, const 
     }
   }
   return SVG_OK;
+}
+
+// ---------------------------------------------------------------------------------------------
+// svg_layer without a workspace argument: its scratch is a static device array, one copy per
+// device.  Host code never passes the array's name to a kernel (on the host it only stands in
+// for the symbol); it uses the device address looked up with hipGetSymbolAddress.
+// ---------------------------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[SVG_LAYER_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` on each device, once looked up
+
+// The current device's copy of the scratch array; `stream` must belong to that device.
+svg_status noalloc_scratch(void* stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "svg_layer_noalloc (hipGetDevice)");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SVG_ERR_UNSUPPORTED, "svg_layer_noalloc: device %d is beyond the %d devices it serves", dev,
+                kMaxDevices);
+  int sdev = dev;
+  e = hipStreamGetDevice((hipStream_t)stream, &sdev);
+  if (e != hipSuccess) return hip_status(e, "svg_layer_noalloc (hipStreamGetDevice)");
+  if (sdev != dev)
+    return fail(SVG_ERR_INVALID, "svg_layer_noalloc: the stream belongs to device %d, device %d is current", sdev, dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "svg_layer_noalloc (hipGetSymbolAddress)");
+    if (p == nullptr || ((uintptr_t)p & 255u))
+      return fail(SVG_ERR_HIP, "svg_layer_noalloc: scratch symbol at %p is not 256-byte aligned", p);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SVG_OK;
+}
+
+}  // namespace
+
+SVG_API svg_status svg_layer_noalloc(const void* q, const void* k, const void* v, const float* wq, const float* wk,
+                                     float eps, float rope_base, int32_t dt, int32_t dh, int32_t dw, void* qn,
+                                     void* kn, const int32_t* q_idx, int32_t n_q, svg_geom g, svg_windows w,
+                                     float scale, int32_t dense, void* o, float* mse_out, uint8_t* kind_out,
+                                     void* stream) {
+  svg_status s;
+  if ((s = check_geom(g, true)) != SVG_OK) return s;
+  const int32_t S = g.F * g.HH * g.WW;
+  if (!dense) {
+    if (n_q < 1 || n_q > S) return fail(SVG_ERR_INVALID, "n_q=%d must lie in [1, S=%d]", n_q, S);
+    const size_t need = layer_ws_bytes(g, n_q);
+    if (need > SVG_LAYER_NOALLOC_SCRATCH_BYTES)
+      return fail(SVG_ERR_WORKSPACE, "svg_layer_noalloc: this layer needs %zu bytes of scratch, the static array holds %zu",
+                  need, (size_t)SVG_LAYER_NOALLOC_SCRATCH_BYTES);
+  }
+  void* ws = nullptr;
+  if ((s = noalloc_scratch(stream, &ws)) != SVG_OK) return s;
+  return svg_layer(q, k, v, wq, wk, eps, rope_base, dt, dh, dw, qn, kn, q_idx, n_q, g, w, scale, dense, o, mse_out,
+                   kind_out, ws, SVG_LAYER_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 // ---------------------------------------------------------------------------------------------

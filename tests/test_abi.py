@@ -218,3 +218,31 @@ def test_block_path_workspace_and_checks(svg):
     assert L.svg_block_sparse_attn(FAKE, FAKE, FAKE, FAKE, small, 0.125, F2, None, 0, None) == -4
     assert L.svg_block_sparse_attn(FAKE, FAKE, FAKE, FAKE, small, 0.0, F2, FAKE, 1 << 20, None) == -1
     assert L.svg_dense_attn_lse(FAKE, FAKE, FAKE, small, 0.125, F2, None, None) == -1
+
+
+def test_layer_noalloc_rejects_oversized_requests(svg):
+    """svg_layer_noalloc refuses, on the host and before any device call, a layer whose
+    workspace would not fit its static scratch, and a bad sample size."""
+    from ctypes import c_void_p
+    fake = c_void_p(1 << 20)       # aligned, never dereferenced: the checks fail first
+    big = svg.Geom(1, 4096, 1, 8, 8, 128)
+    need = svg.workspace_bytes(svg.OP_LAYER, big, 64)
+    assert need > svg.NOALLOC_SCRATCH_BYTES
+    st = svg.lib.svg_layer_noalloc(fake, fake, fake, None, None, 1e-6, 1e4, 44, 42, 42, None, None, fake, 64, big,
+                                   svg.Windows(1, 2), 0.088, 0, fake, fake, fake, None)
+    assert st == -4 and b"scratch" in svg.lib.svg_last_error()
+    small = svg.Geom(1, 2, 2, 8, 8, 128)
+    assert svg.workspace_bytes(svg.OP_LAYER, small, 64) <= svg.NOALLOC_SCRATCH_BYTES
+    st = svg.lib.svg_layer_noalloc(fake, fake, fake, None, None, 1e-6, 1e4, 44, 42, 42, None, None, fake, 0, small,
+                                   svg.Windows(1, 2), 0.088, 0, fake, fake, fake, None)
+    assert st == -1
+    bad_d = svg.Geom(1, 2, 2, 8, 8, 96)
+    st = svg.lib.svg_layer_noalloc(fake, fake, fake, None, None, 1e-6, 1e4, 32, 32, 32, None, None, fake, 64, bad_d,
+                                   svg.Windows(1, 2), 0.088, 0, fake, fake, fake, None)
+    assert st == -2
+
+
+def test_noalloc_scratch_size_matches_header(svg):
+    text = open(HEADER).read()
+    m = re.search(r"#define SVG_LAYER_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == svg.NOALLOC_SCRATCH_BYTES
