@@ -92,7 +92,12 @@ typedef struct {
  * q, k:            bf16 [B][H][S][D] frame-major inputs.
  * q_out, k_out:    bf16 [B][H][S][D] outputs; may equal q / k (in place).
  * wq, wk:          fp32 [D] device arrays, shared by all heads.
- * eps > 0, rope_base > 0; dt, dh, dw >= 0, even, dt + dh + dw == D.
+ * eps > 0, rope_base > 0; dt, dh, dw >= 0, even, dt + dh + dw == D (svg_rope_split gives the
+ *   split used by default).
+ * The rotation tables are built on the device, once per workgroup, from rope_base alone: each
+ *   inverse frequency rope_base^(-2j/n) is an fp64 power, each angle pos * freq is formed in
+ *   fp64 and reduced to [-pi, pi], and its cosine and sine are taken in fp32 (within about one
+ *   fp32 ulp).  The caller therefore passes no cos/sin tables.
  * Arithmetic in fp32, round-to-nearest-even on store.  V is not touched.
  */
 svg_status svg_qknorm_rope(const void* q, const void* k, void* q_out, void* k_out,
@@ -353,6 +358,14 @@ svg_status svg_block_select(const float* mass, svg_geom g, float coverage, uint8
  */
 svg_status svg_block_sparse_attn(const void* q, const void* k, const void* v, const uint8_t* sel, svg_geom g,
                                  float scale, void* o, void* ws, size_t ws_bytes, void* stream);
+
+/* The default widths of the frame / grid-row / grid-column slices of the head dim for RoPE:
+ * dt = D - 4*floor(D/6), dh = dw = 2*floor(D/6) (44/42/42 at D = 128, 24/20/20 at D = 64), the
+ * near-even split into three even slices.  SVG_ERR_INVALID for D < 6 or odd D, or NULL outputs. */
+svg_status svg_rope_split(int32_t D, int32_t* dt, int32_t* dh, int32_t* dw);
+
+/* The default softmax scale 1/sqrt(D) (0 for D <= 0). */
+float svg_default_scale(int32_t D);
 
 /* Bytes of workspace a call needs (0 for an invalid request); n is the sample size n_q for
  * SVG_OP_PROFILE and SVG_OP_LAYER, the cluster count for SVG_OP_KMEANS and SVG_OP_CLUSTER_ATTN. */

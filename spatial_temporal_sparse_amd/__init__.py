@@ -11,7 +11,6 @@ in frame-major order (t = f*HH*WW + y*WW + x) unless a function says token-major
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 from typing import Optional, Tuple
 
@@ -85,6 +84,8 @@ _SIGNATURES = {
                                    _c_vp]),
     "svg_workspace_bytes": (ctypes.c_size_t, [_c_i32, ctypes.POINTER(Geom), _c_i32]),
     "svg_tile_shape": (None, [ctypes.POINTER(_c_i32), ctypes.POINTER(_c_i32)]),
+    "svg_rope_split": (_st, [_c_i32, ctypes.POINTER(_c_i32), ctypes.POINTER(_c_i32), ctypes.POINTER(_c_i32)]),
+    "svg_default_scale": (ctypes.c_float, [_c_i32]),
     "svg_status_string": (ctypes.c_char_p, [_c_i32]),
     "svg_last_error": (ctypes.c_char_p, []),
 }
@@ -147,13 +148,15 @@ def _shape(g: Geom):
 
 
 def default_scale(D: int) -> float:
-    return 1.0 / math.sqrt(D)
+    """The library's default softmax scale (svg_default_scale)."""
+    return float(lib.svg_default_scale(int(D)))
 
 
 def rope_split(D: int) -> Tuple[int, int, int]:
-    """Frame / row / column slice widths of the head dim: D - 4*floor(D/6), 2*floor(D/6), 2*floor(D/6)."""
-    third = 2 * (D // 6)
-    return D - 2 * third, third, third
+    """The library's default frame / row / column slice widths of the head dim (svg_rope_split)."""
+    dt, dh, dw = _c_i32(), _c_i32(), _c_i32()
+    _check(lib.svg_rope_split(int(D), ctypes.byref(dt), ctypes.byref(dh), ctypes.byref(dw)))
+    return dt.value, dh.value, dw.value
 
 
 def workspace_bytes(op: int, g: Geom, n_q: int = 0) -> int:

@@ -746,6 +746,18 @@ SVG_API size_t svg_workspace_bytes(int32_t op, const svg_geom* g, int32_t n_q) {
   return 0;
 }
 
+SVG_API svg_status svg_rope_split(int32_t D, int32_t* dt, int32_t* dh, int32_t* dw) {
+  if (dt == nullptr || dh == nullptr || dw == nullptr) return fail(SVG_ERR_INVALID, "svg_rope_split: NULL output");
+  if (D < 6 || (D & 1)) return fail(SVG_ERR_INVALID, "svg_rope_split: D=%d must be even and >= 6", D);
+  const int32_t third = 2 * (D / 6);
+  *dt = D - 2 * third;
+  *dh = third;
+  *dw = third;
+  return SVG_OK;
+}
+
+SVG_API float svg_default_scale(int32_t D) { return D > 0 ? (float)(1.0 / std::sqrt((double)D)) : 0.f; }
+
 SVG_API void svg_tile_shape(int32_t* bm, int32_t* bn) {
   if (bm) *bm = svg::ATTN_BM;
   if (bn) *bn = svg::ATTN_BN;

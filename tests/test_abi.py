@@ -246,3 +246,18 @@ def test_noalloc_scratch_size_matches_header(svg):
     text = open(HEADER).read()
     m = re.search(r"#define SVG_LAYER_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
     assert m and int(m.group(1)) << int(m.group(2)) == svg.NOALLOC_SCRATCH_BYTES
+
+
+def test_rope_split_and_default_scale(svg):
+    assert svg.rope_split(128) == (44, 42, 42) and svg.rope_split(64) == (24, 20, 20)
+    assert svg.rope_split(6) == (2, 2, 2) and svg.rope_split(12) == (4, 4, 4)
+    for D in range(6, 257, 2):
+        dt, dh, dw = svg.rope_split(D)
+        assert dt + dh + dw == D and dt % 2 == dh % 2 == dw % 2 == 0 and dh == dw and 0 <= dt - dh <= 4
+    import ctypes
+    x = ctypes.c_int32()
+    for bad in (4, 7, 0, -2):
+        assert svg.lib.svg_rope_split(bad, ctypes.byref(x), ctypes.byref(x), ctypes.byref(x)) == -1
+    assert svg.lib.svg_rope_split(128, None, ctypes.byref(x), ctypes.byref(x)) == -1
+    assert abs(svg.default_scale(128) - 128 ** -0.5) < 1e-8 and svg.default_scale(64) == 0.125
+    assert svg.default_scale(0) == 0.0
