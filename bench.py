@@ -34,6 +34,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_hunyuan720p_traffic.json
 CLUSTER_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "cluster_attn_hunyuan720p_svg2_traffic.json")
 BLOCK_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "block_attn_hunyuan720p_blocks_traffic.json")
 MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_busy_hunyuan720p.json")
+HBM_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_kernels_hunyuan720p_traffic.json")
 
 
 def log(msg):
@@ -50,6 +51,10 @@ def parse():
                     help="layout transformation of temporal heads inside the attention kernel, or as separate "
                          "permute / unpermute passes")
     ap.add_argument("--no-compare", action="store_true", help="do not also time the other layout")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the CPU oracle leg (for profiler runs, which only need the GPU kernels)")
+    ap.add_argument("--no-isolated", action="store_true",
+                    help="skip the isolated timing of the HBM-bound kernels (MALL flushed before every launch)")
     ap.add_argument("--workload", choices=("hunyuan720p_step", "cogvideox", "wan", "hunyuan720p_svg2",
                                            "hunyuan720p_blocks"),
                     default="hunyuan720p_step",
@@ -99,46 +104,62 @@ def token_flops(kind_np, g, w_f, w_p):
     return 4.0 * g.D * sum(per[int(k)] for k in kind_np.ravel())
 
 
-def kernel_sha():
-    """Hash of the attention kernel's code (comments and whitespace ignored), which the stored
-    traffic counters were taken on."""
-    import re
-    h = hashlib.sha256()
-    for f in ("attn_fwd.hip", "svg_internal.h"):
-        with open(os.path.join(ROOT, "spatial_temporal_sparse_amd", "csrc", f)) as fh:
-            text = fh.read()
-        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
-        text = re.sub(r"//[^\n]*", " ", text)
-        h.update(" ".join(text.split()).encode())
-    return h.hexdigest()[:16]
+def kernel_sha(group="attn_fwd"):
+    """Hash of the kernel code (comments and whitespace ignored) that stored counter figures were
+    taken on (see rocprof_report.py, which writes them)."""
+    import rocprof_report
+    return rocprof_report.source_sha(group)
+
+
+def _load_json(path):
+    try:
+        with open(path) as fh:
+            return json.load(fh)
+    except (OSError, ValueError):
+        return None
 
 
 def measured_traffic(path=TRAFFIC_FILE):
-    """HBM bytes per launch of the attention kernel from the committed counter runs, if they
-    were taken on the current kernel source; else None."""
-    try:
-        with open(path) as fh:
-            t = json.load(fh)
-    except (OSError, ValueError):
-        return None
-    if t.get("kernel_sha") != kernel_sha():
+    """HBM bytes per launch of an attention kernel from the committed counter runs, if they were
+    taken on the current kernel source; else None."""
+    t = _load_json(path)
+    if t is None or t.get("kernel_sha") != kernel_sha():
         return None
     return t.get("bytes_per_launch")
 
 
-def measured_mfma(kernel):
-    """MFMA busy fraction and clock of an attention kernel at 720p from the committed counter
-    runs (SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE), if they were taken on the current kernel
-    source; else an empty dict."""
-    try:
-        with open(MFMA_FILE) as fh:
-            t = json.load(fh)
-    except (OSError, ValueError):
+def measured_hbm_traffic():
+    """HBM bytes per launch of the norm/RoPE, profiling and layout-transformation kernels from the
+    committed counter runs, if taken on the current source; else {}."""
+    t = _load_json(HBM_TRAFFIC_FILE)
+    if t is None or t.get("kernel_sha") != kernel_sha("hbm"):
         return {}
-    k = t.get("kernels", {}).get(kernel)
-    if t.get("kernel_sha") != kernel_sha() or k is None:
+    return {k: {"bytes_per_launch": round(v["bytes_per_launch"]), "algorithmic_bytes": v["algorithmic_bytes"]}
+            for k, v in t.get("kernels", {}).items()}
+
+
+def measured_mfma(which):
+    """MFMA busy fraction and clock of the attention kernel at 720p from the committed counter runs
+    (SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE), if taken on the current source; else {}."""
+    t = _load_json(MFMA_FILE)
+    if t is None or t.get("kernel_sha") != kernel_sha():
+        return {}
+    k = t.get("kernels", {}).get(which)
+    if k is None:
         return {}
     return {"mfma_busy": round(k["mfma_busy"], 3), "clock_ghz": round(k["clock_ghz"], 2)}
+
+
+def host_cores():
+    """CPU counts of this host: all cores, the ones this process may run on, and the BLAS
+    threads numpy's matrix products use (the threads the oracle actually runs on)."""
+    affinity = len(os.sched_getaffinity(0))
+    try:
+        import threadpoolctl
+        blas = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
+    except Exception:  # threadpoolctl missing: numpy's BLAS defaults to the affinity size
+        blas = affinity
+    return {"cores": int(blas), "cpu_count": os.cpu_count(), "affinity": affinity, "blas_threads": int(blas)}
 
 
 def cpu_baseline(q, k, v, kinds, g, w_f, w_p):
@@ -146,11 +167,7 @@ def cpu_baseline(q, k, v, kinds, g, w_f, w_p):
     and one temporal head against all S keys; token-level FLOPs / wall time."""
     import numpy as np
     import oracle.svg_oracle as O
-    try:
-        import threadpoolctl
-        threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
-    except Exception:  # threadpoolctl missing: report the affinity size
-        threads = len(os.sched_getaffinity(0))
+    hc = host_cores()
     heads = [int(np.argmax(kinds == 0)), int(np.argmax(kinds == 1))]
     rng = np.random.default_rng(123)
     rows = np.sort(rng.choice(g.S, 6144, replace=False))
@@ -166,7 +183,7 @@ def cpu_baseline(q, k, v, kinds, g, w_f, w_p):
         elapsed += time.perf_counter() - t0
         m = O.mask_rows(kind, rows, g.S, g.P, w_f, w_p)
         flops += 4.0 * g.D * float(m.sum())
-    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", **hc, "kind": "oracle",
             "sample": "fp64 numpy oracle, sparse attention of 6144 sampled query rows of one spatial and one "
                       f"temporal head of the layer (S={g.S}, D={g.D}) against all keys; token-level FLOPs",
             "seconds": round(elapsed, 2)}
@@ -267,11 +284,7 @@ def cluster_cpu_baseline(q, k, v, lq, lk, sel, D):
     head of the layer (given the GPU's clusters and selection); token-level FLOPs / wall time."""
     import numpy as np
     import oracle.svg2_oracle as O2
-    try:
-        import threadpoolctl
-        threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
+    hc = host_cores()
     f64 = lambda t: t.detach().cpu().double().numpy()
     S = q.shape[2]
     rows = np.sort(np.random.default_rng(321).choice(S, 4096, replace=False))
@@ -282,7 +295,7 @@ def cluster_cpu_baseline(q, k, v, lq, lk, sel, D):
     O2.semantic_attention_rows(qh, kh, vh, rows, lqh, lkh, s, 1.0 / math.sqrt(D))
     el = time.perf_counter() - t0
     pairs = float(O2.semantic_mask(lqh[rows], lkh, s).sum())
-    return {"value": 4.0 * D * pairs / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    return {"value": 4.0 * D * pairs / el / 1e12, "unit": "TFLOP/s", **hc, "kind": "oracle",
             "sample": f"fp64 numpy oracle, attention over the selected clusters of 4096 sampled query rows of one "
                       f"head (S={S}, D={D}) given the GPU's clusters and selection; token-level FLOPs",
             "seconds": round(el, 2)}
@@ -392,11 +405,12 @@ def cluster_bench(args):
         "roofline": {"bound": "mfma", "kernel": f"cluster_attn_kernel<{D}>", "achieved": round(attn_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(CLUSTER_TRAFFIC_FILE),
-                     **measured_mfma("cluster_attn_kernel<128>, 720p clustering layer"),
+                     **measured_mfma("cluster_attn"),
                      "note": "computed-tile FLOPs over the svg_cluster_attn call (key lists + attention kernel)"},
     }
-    log("[bench] timing the CPU oracle on a bounded sample")
-    result["cpu_baseline"] = cluster_cpu_baseline(q, k, v, ly.cq.labels, ly.ck.labels, ly.sel, D)
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cluster_cpu_baseline(q, k, v, ly.cq.labels, ly.ck.labels, ly.sel, D)
     print(json.dumps(result), flush=True)
 
 
@@ -405,11 +419,7 @@ def block_cpu_baseline(q, k, v, sel, D):
     (given the GPU's choice); token-level FLOPs / wall time."""
     import numpy as np
     import oracle.adaspa_oracle as A
-    try:
-        import threadpoolctl
-        threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
+    hc = host_cores()
     f64 = lambda t: t.detach().cpu().double().numpy()
     S = q.shape[2]
     rows = np.sort(np.random.default_rng(321).choice(S, 4096, replace=False))
@@ -419,7 +429,7 @@ def block_cpu_baseline(q, k, v, sel, D):
     A.block_sparse_attention_rows(qh, kh, vh, s, rows, 1.0 / math.sqrt(D))
     el = time.perf_counter() - t0
     pairs = float(A.block_token_mask(s, rows, S).sum())
-    return {"value": 4.0 * D * pairs / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    return {"value": 4.0 * D * pairs / el / 1e12, "unit": "TFLOP/s", **hc, "kind": "oracle",
             "sample": f"fp64 numpy oracle, attention over the chosen blocks of 4096 sampled query rows of one head "
                       f"(S={S}, D={D}) given the GPU's block choice; token-level FLOPs",
             "seconds": round(el, 2)}
@@ -555,12 +565,60 @@ def block_bench(args):
         "roofline": {"bound": "mfma", "kernel": f"block_attn_kernel<{D}>", "achieved": round(attn_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(BLOCK_TRAFFIC_FILE),
-                     **measured_mfma("block_attn_kernel<128>, 720p block-sparse layer"),
+                     **measured_mfma("block_attn"),
                      "note": "computed-tile FLOPs over the svg_block_sparse_attn call (block lists + attention kernel)"},
     }
-    log("[bench] timing the CPU oracle on a bounded sample")
-    result["cpu_baseline"] = block_cpu_baseline(q, k, v, b["sel"], D)
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = block_cpu_baseline(q, k, v, b["sel"], D)
     print(json.dumps(result), flush=True)
+
+
+def isolated_hbm(svg, layer, bufs, norm, g, wl, reps=20):
+    """The HBM-bound kernels one at a time on one layer's inputs, each launch preceded by a
+    512 MiB write that evicts the 256 MB Infinity Cache (MALL), so that no launch finds its
+    inputs cached by the one before: median and min over `reps` launches, and the algorithmic
+    bytes per launch."""
+    import numpy as np
+    import torch
+    q, k, v, idx = layer
+    F, HH, WW, w_f, w_p = g.F, g.HH, g.WW, wl.w_f, wl.w_p
+    svg.qknorm_rope(q, k, norm[0], norm[1], F, HH, WW, wl.eps, wl.rope_base, q_out=bufs.qn, k_out=bufs.kn)
+    svg.profile_heads(bufs.qn, bufs.kn, v, idx, F, HH, WW, w_f, w_p, mse=bufs.mse, kind=bufs.kind, ws=bufs.ws_profile)
+    n_tmp = int((bufs.kind == 1).sum().item())
+    row = g.S * g.D * 2
+    BH = g.B * g.H
+
+    def permute_qkv():
+        for src, dst in ((bufs.qn, bufs.qt), (bufs.kn, bufs.kt), (v, bufs.vt)):
+            svg.permute(src, F, HH, WW, bufs.kind, svg.TEMPORAL, out=dst)
+
+    ops = {
+        "qknorm_rope": (lambda: svg.qknorm_rope(q, k, norm[0], norm[1], F, HH, WW, wl.eps, wl.rope_base,
+                                                q_out=bufs.qn, k_out=bufs.kn), 4 * BH * row),
+        "profile_heads": (lambda: svg.profile_heads(bufs.qn, bufs.kn, v, idx, F, HH, WW, w_f, w_p, mse=bufs.mse,
+                                                    kind=bufs.kind, ws=bufs.ws_profile), 2 * BH * row),
+        "permute_qkv": (permute_qkv, 6 * n_tmp * row),
+        "unpermute": (lambda: svg.unpermute(bufs.ot, F, HH, WW, bufs.kind, svg.TEMPORAL, out=bufs.o), 2 * n_tmp * row),
+    }
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=q.device)
+    out = {}
+    for name, (fn, nbytes) in ops.items():
+        fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for i in range(reps):
+            flush.fill_(i & 0xFF)
+            ev[i][0].record()
+            fn()
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        ms = np.array([a.elapsed_time(b) for a, b in ev])
+        med = float(np.median(ms))
+        out[name] = {"ms_median": round(med, 4), "ms_min": round(float(ms.min()), 4), "bytes": int(nbytes),
+                     "gbs_median": round(nbytes / (med * 1e-3) / 1e9, 1),
+                     "frac_of_peak_median": round(nbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)}
+    del flush
+    return out
 
 
 def main():
@@ -667,6 +725,8 @@ def main():
 
     ms_per_step, stage = timed(args.layout)
     stage_ms = {n: float(stage[:, j].mean()) for j, n in enumerate(names)}
+    stage_med = {n: round(float(np.median(stage[:, j])), 4) for j, n in enumerate(names)}
+    stage_min = {n: round(float(stage[:, j].min()), 4) for j, n in enumerate(names)}
     other = "explicit" if args.layout == "fused" else "fused"
     compare = None
     if not args.no_compare:
@@ -729,6 +789,8 @@ def main():
                    "B": g.B, "H": g.H, "F": g.F, "HH": g.HH, "WW": g.WW, "S": S, "D": D, "w_f": w_f, "w_p": w_p,
                    "n_q": wl.n_q, "layers": L, "tile": [bm, bn], "parallelism": "single GPU"},
         "sparse_attn_ms": round(float(attn_ms.mean()), 4),
+        "sparse_attn_ms_median": round(float(np.median(attn_ms)), 4),
+        "sparse_attn_ms_min": round(float(attn_ms.min()), 4),
         "sparse_attn_tflops": round(attn_tflops, 2),
         "sparse_attn_frac_of_bf16_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
         "tile_tflop_per_layer": round(tile_per_launch / 1e12, 4),
@@ -739,18 +801,29 @@ def main():
         "speedup_vs_dense_step": round((stage_ms["qknorm_rope"] + dense_ms) / ms_per_step, 3),
         "profile_over_attn": round(stage_ms["profile_heads"] / stage_ms["sparse_attn"], 4),
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "stage_ms_median": stage_med,
+        "stage_ms_min": stage_min,
         "compare": compare,
         "hbm_gbs": {k: round(v, 1) for k, v in hbm.items()},
         "hbm_frac_of_peak": {k: round(v / PEAK_HBM_GBS, 3) for k, v in hbm.items()},
         "roofline": {"bound": "mfma", "kernel": f"attn_fwd_kernel<{D}>", "achieved": round(attn_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic,
-                     **(measured_mfma("attn_fwd_kernel<128>, sparse 720p layer") if headline else {})},
+                     **(measured_mfma("attn_fwd sparse") if headline else {})},
     }
-    log("[bench] timing the CPU oracle on a bounded sample")
-    qn = bufs.qn  # the last layer's normalised Q/K; pair them with that layer's V
-    last = (args.steps - 1) % L
-    result["cpu_baseline"] = cpu_baseline(qn, bufs.kn, layers[last][2], kinds[last], g, w_f, w_p)
+    hbm_traffic = measured_hbm_traffic() if headline else {}
+    if hbm_traffic:
+        result["hbm_traffic"] = hbm_traffic
+    if not args.no_isolated:
+        log("[bench] HBM-bound kernels one at a time, the MALL flushed before every launch")
+        result["hbm_isolated"] = isolated_hbm(svg, layers[0], bufs, norm, g, wl)
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        # the last timed layer's normalised Q/K (recomputed: the isolated leg overwrote them)
+        last = (args.steps - 1) % L
+        q, k, v, _ = layers[last]
+        svg.qknorm_rope(q, k, norm[0], norm[1], F, HH, WW, wl.eps, wl.rope_base, q_out=bufs.qn, k_out=bufs.kn)
+        result["cpu_baseline"] = cpu_baseline(bufs.qn, bufs.kn, v, kinds[last], g, w_f, w_p)
     print(json.dumps(result), flush=True)
 
 
