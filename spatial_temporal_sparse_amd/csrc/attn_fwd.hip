@@ -28,8 +28,9 @@
 //                                order inside each 16-key step is permuted identically on
 //                                both operands, which leaves the contraction unchanged.
 //   The O^T accumulator again holds one query per lane, so the online-softmax rescale is a
-//   per-lane scalar.  It is applied lazily: the running max only moves when a tile's max
-//   exceeds it by more than 8 (log2 units), which bounds p by 2^8 and skips most rescales.
+//   per-lane scalar.  It is applied lazily: the reference moves only when a weight would
+//   exceed 2^8, which the tile's row sum reveals (see phase_softmax), so most tiles need
+//   neither a rescale nor a maximum.
 // exp2 with log2(e) folded into the softmax scale; fp32 accumulation; P rounded to bf16 for
 // the PV product; output divided by the row sum of those bf16 weights (so they sum to 1) and
 // rounded to bf16 (round-to-nearest-even).
@@ -40,7 +41,6 @@ namespace svg {
 namespace {
 
 constexpr int BN = ATTN_BN;       // keys per tile
-constexpr float RESCALE_SLACK = 8.0f;
 
 // Workgroups are handed to the 8 XCDs round-robin by index, and each XCD has its own L2.
 // Consecutive query blocks of a head read (almost) the same key/value tiles in the same
@@ -104,14 +104,14 @@ __global__ void head_order_kernel(const uint8_t* __restrict__ kind, int32_t* __r
 // its MFMAs are few and long, and the exponentials fill the issue slots between them.
 // Every phase runs the same code for every tile index: a tile outside a group's range is a
 // boundary tile whose element mask empties it (P^T = 0; running max and sum unchanged).
-// The HBM -> LDS copies are issued at the end of the M phases, once the issuing group's LDS
-// reads are done, and split between the groups: after M(j), group A copies K(t_{j+1}) (into
-// the K buffer M(j-1) read) and group B copies V(t_{j+1}) (into the V buffer of V(t_{j-2})).
-// Each group waits for its copies at the end of its next X phase and the barrier after it
-// publishes them, one phase (K) or two phases (V) before their first reader.  So no copy is
-// in flight during an M phase; each M phase still starts with an explicit wait on vector
-// memory (free at run time) so that the compiler knows it and counts the LDS waits instead
-// of draining them.  After that wait at the end of its X phase, a group reads the first V^T
+// The HBM -> LDS copies are split between the groups and issued at the start of each group's
+// vector phase: in X(j), the phase after its M(j), group A copies K(t_{j+1}) (into the K
+// buffer M(j-1) read) and group B copies V(t_{j+1}) (into the V buffer of V(t_{j-2})).  A copy
+// holds its wavefront at issue, and the vector phases have the slack for it.  Each group
+// waits for its copies at the end of that X phase and the barrier after it publishes them,
+// one phase (K) or two phases (V) before their first reader.  So no copy is in flight during
+// an M phase; each M phase still starts with an explicit wait on vector memory (free at run
+// time) so that the compiler knows it and counts the LDS waits instead of draining them.  After that wait at the end of its X phase, a group reads the first V^T
 // operand of its next M phase: that V tile was published a phase earlier.  The K buffers are
 // two distinct LDS objects and the phase loop is unrolled by four, so every K access names one
 // of them.
@@ -127,6 +127,7 @@ struct RowState {
   bf16x8 pb[BN / 16];        // P^T of the previous tile as bf16 MFMA operands (16 keys each)
   float m_ref;               // reference max (log2 units) of oacc / l_run
   float l_run;               // this lane's share of the row sum
+  bool m_set;                // m_ref has been set from an allowed key (same in both halves of a row)
 };
 
 // the value of x held by lane l^32
@@ -239,48 +240,15 @@ __device__ __forceinline__ void phase_m(RowState<D>& st, const bf16x8 (&qf)[D / 
   order_m_phase<0, (BN / 16) * (D / 32), 2 * (D / 16), SVG_ATTN_M_AHEAD, 0>();
 }
 
-// Exact token mask (boundary tiles), online softmax with lazy rescaling, bf16 P^T operands.
+
+// bf16 P^T operands from the lane's 32 weights, and the row sums of those bf16 weights (the
+// ones the PV product uses), two at a time (v_dot2_f32_bf16 against (1, 1)), in two chains
 template <int D>
-__device__ __forceinline__ void phase_softmax(RowState<D>& st, int32_t k0, bool edge, int32_t my_lo, int32_t my_hi,
-                                              float c, int hh) {
-  constexpr int NDB = D / 32;
-  if (edge) {
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int32_t key = k0 + blk * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-        st.sacc[blk][r] = (key < my_lo || key >= my_hi) ? -INFINITY : st.sacc[blk][r];
-      }
-  }
-  float mx = -INFINITY;
-#pragma unroll
-  for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st.sacc[blk][r]);
-  mx = max_halves(mx) * c;
-  const bool bump = mx > st.m_ref + RESCALE_SLACK;
-  if (__any(bump)) {
-    const float m_new = bump ? mx : st.m_ref;
-    const float alpha = (st.m_ref == -INFINITY) ? 0.f : exp2f(st.m_ref - m_new);
-    st.l_run *= alpha;
-#pragma unroll
-    for (int j = 0; j < NDB; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st.oacc[j][r] *= alpha;
-    st.m_ref = m_new;
-  }
-  const float m_use = (st.m_ref == -INFINITY) ? 0.f : st.m_ref;
-#pragma unroll
-  for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) st.sacc[blk][r] = __builtin_amdgcn_exp2f(fmaf(st.sacc[blk][r], c, -m_use));
+__device__ __forceinline__ float pack_weights(RowState<D>& st, const float (&p)[2][16]) {
 #pragma unroll
   for (int s = 0; s < BN / 16; ++s)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) st.pb[s][e] = (bf16)st.sacc[s >> 1][8 * (s & 1) + e];
-  // row sum of the bf16 weights the PV product uses, two at a time (v_dot2_f32_bf16 against
-  // (1, 1)), in two independent chains
+    for (int e = 0; e < 8; ++e) st.pb[s][e] = (bf16)p[s >> 1][8 * (s & 1) + e];
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
   float rs0 = 0.f, rs1 = 0.f;
@@ -292,7 +260,89 @@ __device__ __forceinline__ void phase_softmax(RowState<D>& st, int32_t k0, bool 
     rs0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(q, q, 4, 5), one, rs0, false);
     rs1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(q, q, 6, 7), one, rs1, false);
   }
-  st.l_run += rs0 + rs1;
+  return rs0 + rs1;
+}
+
+// Exact token mask (boundary tiles), online softmax, bf16 P^T operands.
+//
+// The weights are taken against a reference m_ref (log2 units) that only moves when it must.
+// The first tile holding an allowed key of the row sets it to that tile's maximum score; after
+// that the fast path exponentiates against the current reference and checks the lane's sum of
+// the bf16 weights.  A sum of at most 2^8 means no weight exceeds 2^8 (and none overflowed);
+// otherwise the slow path takes the tile's true maximum, moves the reference up to it
+// (rescaling O and the sum) and exponentiates again.  So the reference always lies between
+// the row's largest score so far minus 8 and that score, the bound the lazy rescaling of the
+// running maximum gave, and a tile costs one compare on the sum instead of a 32-score
+// maximum and its cross-lane exchange.
+template <int D>
+__device__ __forceinline__ void phase_softmax(RowState<D>& st, int32_t k0, bool edge, int32_t my_lo, int32_t my_hi,
+                                              float c, int hh) {
+  constexpr int NDB = D / 32;
+  bool has_keys = true;
+  if (edge) {
+    // element (blk, r) holds key k0 + 4 hh + off, off = 32 blk + 8 (r >> 2) + (r & 3); the
+    // lane's allowed offsets are [lo, hi).  Each bound costs a compare and a select per score,
+    // and only where some lane of the wavefront needs it.
+    const int32_t lo = my_lo - k0 - 4 * hh, hi = my_hi - k0 - 4 * hh;
+    has_keys = lo < BN && hi > 0 && lo < hi;
+    if (__any(lo > 0)) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int32_t off = blk * 32 + 8 * (r >> 2) + (r & 3);
+          st.sacc[blk][r] = off < lo ? -INFINITY : st.sacc[blk][r];
+        }
+    }
+    if (__any(hi < BN)) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int32_t off = blk * 32 + 8 * (r >> 2) + (r & 3);
+          st.sacc[blk][r] = off >= hi ? -INFINITY : st.sacc[blk][r];
+        }
+    }
+  }
+  // x = scale * log2(e) * s - m_ref in place, then the exponentials: each exponential's input
+  // was formed 32 instructions earlier, and the slow path recovers the scores from x
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st.sacc[blk][r] = fmaf(st.sacc[blk][r], c, -st.m_ref);
+  __builtin_amdgcn_sched_barrier(0);
+  float p[2][16];
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) p[blk][r] = __builtin_amdgcn_exp2f(st.sacc[blk][r]);
+  float rs = pack_weights<D>(st, p);
+  if (__any(!(rs <= 256.f) | (!st.m_set & has_keys))) {
+    // the tile's largest x over both halves of the row (-inf: no allowed key)
+    float mx = -INFINITY;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st.sacc[blk][r]);
+    mx = max_halves(mx);
+    // the first allowed key sets the reference; later it only moves up
+    const bool set_now = !st.m_set && mx > -INFINITY;
+    const float up = (mx > 0.f || set_now) ? mx : 0.f;
+    const float alpha = st.m_set ? __builtin_amdgcn_exp2f(-up) : 0.f;
+    st.l_run *= alpha;
+#pragma unroll
+    for (int j = 0; j < NDB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.oacc[j][r] *= alpha;
+    st.m_ref += up;
+    st.m_set = st.m_set || set_now;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) p[blk][r] = __builtin_amdgcn_exp2f(st.sacc[blk][r] - up);
+    rs = pack_weights<D>(st, p);
+  }
+  st.l_run += rs;
 }
 
 // Workgroup barrier without a memory fence.  The only data one wavefront hands another
@@ -488,7 +538,8 @@ __device__ __forceinline__ void pp_attention(const Src& src, const bf16* __restr
     for (int r = 0; r < 16; ++r) st.oacc[j][r] = 0.f;
 #pragma unroll
   for (int s = 0; s < BN / 16; ++s) st.pb[s] = bf16x8{};
-  st.m_ref = -INFINITY;
+  st.m_ref = 0.f;
+  st.m_set = false;
   st.l_run = 0.f;
   // M(0) reads V(t_{-1}) from Vb[2] with P^T = 0: zero it so that the product is exactly zero
   for (int o = tid; o < BN * D / 8; o += PP_NT) reinterpret_cast<u32x4*>(Vb[2])[o] = u32x4{0u, 0u, 0u, 0u};
@@ -542,57 +593,60 @@ __device__ __forceinline__ void pp_attention(const Src& src, const bf16* __restr
       }
     };
   };
+  // The copies of tile t_{j+1} are issued at the start of the issuing group's vector phase
+  // X(j), the phase after its M(j): group A copies K into the K buffer M(j-1) read, group B
+  // copies V into the V buffer of V(t_{j-2}), which PV(j-2) read in M(j-1).
   auto copy_k = [&](int32_t j, bf16* kdst) {
-    if (j + 1 < T) pp_load<D>(K, kdst, wig, lane, false, rows_of(j));
+    if (j >= 0 && j + 1 < T) pp_load<D>(K, kdst, wig, lane, false, rows_of(j));
   };
   auto copy_v = [&](int32_t j) {
-    if (j + 1 < T) pp_load<D>(V, Vb[(j + 1) % 3], wig, lane, true, rows_of(j));
+    if (j >= 0 && j + 1 < T) pp_load<D>(V, Vb[(j + 1) % 3], wig, lane, true, rows_of(j));
   };
   auto vbuf = [&](int32_t j) { return Vb[(j + 3) % 3]; };   // V(t_j), j >= -1
 
   const int32_t n_phase = 2 * T + 2;
   for (int32_t m = 0;; ++m) {
-    // phase 4m: A: M(2m) [V(2m-1), K0], copies K(t_{2m+1}) -> K1; B: X(2m-1), its copies retire
+    // phase 4m: A: M(2m) [V(2m-1), K0]; B: copies V(t_{2m}), X(2m-1), its copies retire
     if (grp == 0) {
       do_m(vbuf(2 * m - 1), K0);
-      copy_k(2 * m, K1);
     } else {
+      copy_v(2 * m - 1);
       do_x(2 * m - 1);
       __builtin_amdgcn_s_waitcnt(VMCNT0);
       pre(vbuf(2 * m - 1));
     }
     phase_barrier();
     if (4 * m + 1 >= n_phase) break;
-    // phase 4m+1: A: X(2m), its copies retire; B: M(2m) [V(2m-1), K0], copies V(t_{2m+1})
+    // phase 4m+1: A: copies K(t_{2m+1}) -> K1, X(2m), its copies retire; B: M(2m) [V(2m-1), K0]
     if (grp == 0) {
+      copy_k(2 * m, K1);
       do_x(2 * m);
       __builtin_amdgcn_s_waitcnt(VMCNT0);
       pre(vbuf(2 * m));
     } else {
       do_m(vbuf(2 * m - 1), K0);
-      copy_v(2 * m);
     }
     phase_barrier();
     if (4 * m + 2 >= n_phase) break;
-    // phase 4m+2: A: M(2m+1) [V(2m), K1], copies K(t_{2m+2}) -> K0; B: X(2m), its copies retire
+    // phase 4m+2: A: M(2m+1) [V(2m), K1]; B: copies V(t_{2m+1}), X(2m), its copies retire
     if (grp == 0) {
       do_m(vbuf(2 * m), K1);
-      copy_k(2 * m + 1, K0);
     } else {
+      copy_v(2 * m);
       do_x(2 * m);
       __builtin_amdgcn_s_waitcnt(VMCNT0);
       pre(vbuf(2 * m));
     }
     phase_barrier();
     if (4 * m + 3 >= n_phase) break;
-    // phase 4m+3: A: X(2m+1), its copies retire; B: M(2m+1) [V(2m), K1], copies V(t_{2m+2})
+    // phase 4m+3: A: copies K(t_{2m+2}) -> K0, X(2m+1), its copies retire; B: M(2m+1) [V(2m), K1]
     if (grp == 0) {
+      copy_k(2 * m + 1, K0);
       do_x(2 * m + 1);
       __builtin_amdgcn_s_waitcnt(VMCNT0);
       pre(vbuf(2 * m + 1));
     } else {
       do_m(vbuf(2 * m), K1);
-      copy_v(2 * m + 1);
     }
     phase_barrier();
     if (4 * m + 4 >= n_phase) break;
@@ -613,8 +667,7 @@ __device__ __forceinline__ void pp_attention(const Src& src, const bf16* __restr
         *reinterpret_cast<bf16x4*>(orow + 32 * j + 8 * rq + 4 * hh) = ov;
       }
     if constexpr (LSE) {
-      const float m = st.m_ref == -INFINITY ? 0.f : st.m_ref;
-      if (hh == 0) lse[src.q_row_in(my_q)] = 0.69314718055994531f * (m + __log2f(l_tot));
+      if (hh == 0) lse[src.q_row_in(my_q)] = 0.69314718055994531f * (st.m_ref + __log2f(l_tot));
     }
   }
 }
