@@ -111,7 +111,9 @@ __global__ __launch_bounds__(BM_NT, 4) void block_mass_kernel(BlockMassArgs a) {
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, acc[0][r]);
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[1][r]);
-    if (__any(fmaf(mx, c, -l2) > -40.f)) {
+    const bool live = __any(fmaf(mx, c, -l2) > -40.f);   // the same for every lane of the wavefront
+    float s = 0.f;
+    if (live) {
       if (kend >= BM_KT) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -130,9 +132,10 @@ __global__ __launch_bounds__(BM_NT, 4) void block_mass_kernel(BlockMassArgs a) {
             }
           }
       }
+      // a skipped tile's wavefront sum is exactly 0 and needs no reduction
+      s = sum0 + sum1;
+      for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
     }
-    float s = sum0 + sum1;
-    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
     if (lane == 0) part[buf][wave] = s;
     if (t + 1 < nt) stash(buf ^ 1);
     __syncthreads();
