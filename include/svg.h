@@ -170,7 +170,9 @@ svg_status svg_build_block_mask(const uint8_t* kind, svg_geom g, svg_windows w, 
  * q, k, v, o, qt, kt, vt, ot: bf16 [B][H][S][D]; a mix of NULL and non-NULL token-major
  * pointers is SVG_ERR_INVALID when kind is given (they are ignored when kind is NULL).
  * kind: uint8 [B*H] device array (NULL = every head dense).
- * ws:   >= svg_workspace_bytes(SVG_OP_SPARSE_ATTN, &g, 0) bytes.
+ * ws:   >= svg_workspace_bytes(SVG_OP_SPARSE_ATTN, &g, 0) bytes: the order in which heads
+ *       are processed and the counters workgroups take band items from; two calls in
+ *       flight at once must not share it.
  * S*D*2 bytes (one head) must be below 4 GB, else SVG_ERR_UNSUPPORTED (also svg_dense_attn).
  */
 svg_status svg_sparse_attn(const void* q, const void* k, const void* v,

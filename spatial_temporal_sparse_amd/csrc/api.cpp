@@ -77,7 +77,8 @@ size_t profile_ws_bytes(const svg_geom& g, int32_t n_q) {
          align_up(p.sq_doubles * sizeof(double), 256);
 }
 
-size_t attn_ws_bytes(const svg_geom& g) { return align_up((size_t)g.B * g.H * sizeof(int32_t), 256); }
+// the head order, then the persistent kernel's per-XCD work counters
+size_t attn_ws_bytes(const svg_geom& g) { return align_up((size_t)g.B * g.H * sizeof(int32_t), 256) + 256; }
 
 }  // namespace
 
@@ -297,6 +298,7 @@ static svg_status svg_sparse_attn_impl(const void* q, const void* k, const void*
   a.ot = (svg::bf16*)(ot ? ot : o);
   a.kind = kind;
   a.order = kind ? (int32_t*)ws : nullptr;
+  a.queue = kind ? (int32_t*)((char*)ws + align_up((size_t)g.B * g.H * sizeof(int32_t), 256)) : nullptr;
   a.force_dense = 0;
   a.fused_t = fused ? 1 : 0;
   fill_attn(a, g, w, scale);
@@ -325,6 +327,7 @@ static svg_status svg_dense_attn_impl(const void* q, const void* k, const void* 
   a.o = a.ot = (svg::bf16*)o;
   a.kind = nullptr;
   a.order = nullptr;
+  a.queue = nullptr;
   a.force_dense = 1;
   fill_attn(a, g, svg_windows{0, 0}, scale);
   return hip_status(svg::launch_attention(a, (hipStream_t)stream), "svg_dense_attn");
@@ -639,6 +642,7 @@ SVG_API svg_status svg_dense_attn_lse(const void* q, const void* k, const void* 
   a.o = a.ot = (svg::bf16*)o;
   a.kind = nullptr;
   a.order = nullptr;
+  a.queue = nullptr;
   a.force_dense = 1;
   fill_attn(a, g, svg_windows{0, 0}, scale);
   a.lse = lse;

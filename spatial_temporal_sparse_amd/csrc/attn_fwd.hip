@@ -80,8 +80,11 @@ struct TileLds {
   static __device__ __forceinline__ int swz_v(int r) { return 4 * ((r / RPB) & (CPR / 4 - 1)); }
 };
 
-__global__ void head_order_kernel(const uint8_t* __restrict__ kind, int32_t* __restrict__ order, int32_t BH) {
-  // Heavier heads first (spatial, dense), temporal heads last; stable within a class.
+__global__ void head_order_kernel(const uint8_t* __restrict__ kind, int32_t* __restrict__ order, int32_t BH,
+                                  int32_t* __restrict__ queue) {
+  // Heavier heads first (spatial, dense), temporal heads last; stable within a class.  Also
+  // clears the per-XCD work counters of the persistent kernel.
+  if (queue != nullptr && threadIdx.x < NXCD && blockIdx.x == 0) queue[threadIdx.x] = 0;
   if (threadIdx.x != 0 || blockIdx.x != 0) return;
   int32_t n = 0;
   for (int32_t h = 0; h < BH; ++h)
@@ -673,8 +676,7 @@ __device__ __forceinline__ void pp_attention(const Src& src, const bf16* __restr
 }
 
 template <int D>
-__global__ __launch_bounds__(PP_NT, 1) void attn_fwd_kernel(AttnArgs a, int32_t nqb) {
-  const int32_t item = xcd_item((int32_t)blockIdx.x, (int32_t)gridDim.x);
+__device__ __forceinline__ void band_item(const AttnArgs& a, int32_t nqb, int32_t item) {
   const int32_t rank = item / nqb;
   const int32_t qb = item - rank * nqb;
   const int32_t bh = a.order ? a.order[rank] : rank;
@@ -697,6 +699,37 @@ __global__ __launch_bounds__(PP_NT, 1) void attn_fwd_kernel(AttnArgs a, int32_t 
   else { src.band.divG = a.divP; src.band.G = a.P; src.band.NG = a.F; src.band.w = a.w_f; }
   pp_attention<D>(src, (own_t ? a.qt : a.q) + off, (own_t ? a.kt : a.k) + off, (own_t ? a.vt : a.v) + off,
                   (own_t ? a.ot : a.o) + off, a.S, qb * PP_BM, a.scale);
+}
+
+template <int D>
+__global__ __launch_bounds__(PP_NT, 1) void attn_fwd_kernel(AttnArgs a, int32_t nqb) {
+  band_item<D>(a, nqb, xcd_item((int32_t)blockIdx.x, (int32_t)gridDim.x));
+}
+
+// Up to this many band items per CU the persistent grid below is used: with few items per CU
+// the per-XCD queue evens out the tail (Wan 480p, 40 items per CU: 3-6% faster; CogVideoX,
+// 26 per CU: 1-5%), while with many (HunyuanVideo 720p, 87 per CU) the one-item grid measured
+// 1% faster.
+constexpr int32_t PERSIST_MAX_ITEMS_PER_CU = 48;
+
+// The same work with one workgroup per CU that takes items until none are left.  Workgroup w
+// runs on XCD w % 8 (workgroups reach the XCDs round-robin) and takes the items the one-item
+// kernel would have given that XCD, in the same order, from a per-XCD counter: the k-th item
+// of XCD x is xcd_item(8 k + x).  The next item's index is fetched while the current one runs.
+template <int D>
+__global__ __launch_bounds__(PP_NT, 1) void attn_fwd_persistent_kernel(AttnArgs a, int32_t nqb, int32_t n_items) {
+  __shared__ int32_t next_b;
+  const int32_t x = (int32_t)blockIdx.x % NXCD;
+  if (threadIdx.x == 0) next_b = atomicAdd(&a.queue[x], 1) * NXCD + x;
+  __syncthreads();
+  int32_t b = next_b;
+  while (b < n_items) {
+    __syncthreads();                     // every thread has read next_b
+    if (threadIdx.x == 0) next_b = atomicAdd(&a.queue[x], 1) * NXCD + x;
+    band_item<D>(a, nqb, xcd_item(b, n_items));
+    __syncthreads();
+    b = next_b;
+  }
 }
 
 // One workgroup per (head, query cluster, 256-row tile of that cluster); unused item slots of a
@@ -766,6 +799,8 @@ __global__ __launch_bounds__(PP_NT, 1) void block_attn_kernel(BlockAttnArgs a) {
 // Explicit instantiations, so that the host pass emits every launch stub the launchers use.
 template __global__ void attn_fwd_kernel<128>(AttnArgs, int32_t);
 template __global__ void attn_fwd_kernel<64>(AttnArgs, int32_t);
+template __global__ void attn_fwd_persistent_kernel<128>(AttnArgs, int32_t, int32_t);
+template __global__ void attn_fwd_persistent_kernel<64>(AttnArgs, int32_t, int32_t);
 template __global__ void cluster_attn_kernel<128>(ClusterAttnArgs);
 template __global__ void cluster_attn_kernel<64>(ClusterAttnArgs);
 template __global__ void attn_lse_kernel<128>(AttnArgs, int32_t);
@@ -778,13 +813,30 @@ template __global__ void block_attn_kernel<64>(BlockAttnArgs);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
   const int32_t nqb = (a.S + PP_BM - 1) / PP_BM;
   if (a.order != nullptr && a.kind != nullptr && !a.force_dense) {
-    head_order_kernel<<<1, 64, 0, st>>>(a.kind, a.order, a.BH);
+    head_order_kernel<<<1, 64, 0, st>>>(a.kind, a.order, a.BH, a.queue);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   AttnArgs b = a;
   if (a.kind == nullptr || a.force_dense) b.order = nullptr;
-  const dim3 grid((unsigned)((int64_t)nqb * a.BH));
+  const int32_t n_items = (int32_t)((int64_t)nqb * a.BH);
+  if (b.order != nullptr && b.queue != nullptr) {
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if ((int64_t)n_items <= (int64_t)PERSIST_MAX_ITEMS_PER_CU * cus) {
+      // at least one workgroup per XCD residue, so that every per-XCD counter is drained
+      int32_t g = cus < n_items ? cus : n_items;
+      if (g < NXCD) g = n_items < NXCD ? n_items : NXCD;
+      const dim3 pgrid((unsigned)g);
+      if (a.D == 128) attn_fwd_persistent_kernel<128><<<pgrid, PP_NT, 0, st>>>(b, nqb, n_items);
+      else if (a.D == 64) attn_fwd_persistent_kernel<64><<<pgrid, PP_NT, 0, st>>>(b, nqb, n_items);
+      else return hipErrorInvalidValue;
+      return hipGetLastError();
+    }
+  }
+  const dim3 grid((unsigned)n_items);
   if (a.D == 128) {
     attn_fwd_kernel<128><<<grid, PP_NT, 0, st>>>(b, nqb);
   } else if (a.D == 64) {

@@ -120,6 +120,7 @@ struct AttnArgs {
   bf16 *o, *ot;
   const uint8_t* kind;        // null: all dense
   int32_t* order;             // [BH] head order scratch (null: identity, no kind)
+  int32_t* queue;             // [8] per-XCD work counters of the persistent kernel (null: none)
   int32_t BH, S, F, P, D, w_f, w_p;
   FastDiv divP, divF;
   float scale;

@@ -59,14 +59,15 @@ def test_tile_shape(svg):
 
 def test_workspace_sizes(svg):
     g = svg.Geom(1, 24, 33, 45, 80, 128)
-    assert svg.workspace_bytes(svg.OP_SPARSE_ATTN, g) == 256
+    # the head order (24 int32, padded to 256 bytes), then 256 bytes of per-XCD work counters
+    assert svg.workspace_bytes(svg.OP_SPARSE_ATTN, g) == 512
     ws = svg.workspace_bytes(svg.OP_PROFILE, g, 64)
     assert ws > 0 and ws % 256 == 0
     assert svg.workspace_bytes(svg.OP_PROFILE, g, 0) == 0                  # n_q out of range
     assert svg.workspace_bytes(svg.OP_PROFILE, svg.Geom(1, 24, 33, 45, 80, 96), 64) == 0   # D unsupported
     assert svg.workspace_bytes(99, g, 64) == 0
     # a layer runs profiling and attention one after the other on one workspace
-    assert svg.workspace_bytes(svg.OP_LAYER, g, 64) == max(ws, 256)
+    assert svg.workspace_bytes(svg.OP_LAYER, g, 64) == max(ws, 512)
     assert svg.workspace_bytes(svg.OP_LAYER, g, 0) == 0
 
 
