@@ -576,9 +576,10 @@ def block_bench(args):
 
 def isolated_hbm(svg, layer, bufs, norm, g, wl, reps=20):
     """The HBM-bound kernels one at a time on one layer's inputs, each launch preceded by a
-    512 MiB write that evicts the 256 MB Infinity Cache (MALL), so that no launch finds its
+    512 MiB read that evicts the 256 MB Infinity Cache (MALL), so that no launch finds its
     inputs cached by the one before: median and min over `reps` launches, and the algorithmic
-    bytes per launch."""
+    bytes per launch.  The eviction reads rather than writes, so that the timed launch does
+    not also pay for writing back the eviction's own dirty lines."""
     import numpy as np
     import torch
     q, k, v, idx = layer
@@ -601,13 +602,13 @@ def isolated_hbm(svg, layer, bufs, norm, g, wl, reps=20):
         "permute_qkv": (permute_qkv, 6 * n_tmp * row),
         "unpermute": (lambda: svg.unpermute(bufs.ot, F, HH, WW, bufs.kind, svg.TEMPORAL, out=bufs.o), 2 * n_tmp * row),
     }
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=q.device)
+    flush = torch.ones(128 << 20, dtype=torch.int32, device=q.device)   # 512 MiB
     out = {}
     for name, (fn, nbytes) in ops.items():
         fn()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
         for i in range(reps):
-            flush.fill_(i & 0xFF)
+            flush.sum()
             ev[i][0].record()
             fn()
             ev[i][1].record()

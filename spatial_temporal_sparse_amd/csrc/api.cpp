@@ -174,7 +174,6 @@ static svg_status svg_profile_heads_impl(const void* q, const void* k, const voi
   a.divP = svg::make_fastdiv((uint32_t)a.P);
   a.scale = scale;
   a.nsplit = plan.nsplit;
-  a.keys_per_split = plan.keys_per_split;
   a.part_ml = (float*)ws;
   a.part_o = (float*)((char*)ws + align_up(plan.ml_floats * sizeof(float), 256));
   a.row_sq = (double*)((char*)a.part_o + align_up(plan.o_floats * sizeof(float), 256));

@@ -706,11 +706,11 @@ __global__ __launch_bounds__(PP_NT, 1) void attn_fwd_kernel(AttnArgs a, int32_t 
   band_item<D>(a, nqb, xcd_item((int32_t)blockIdx.x, (int32_t)gridDim.x));
 }
 
-// Up to this many band items per CU the persistent grid below is used: with few items per CU
-// the per-XCD queue evens out the tail (Wan 480p, 40 items per CU: 3-6% faster; CogVideoX,
-// 26 per CU: 1-5%), while with many (HunyuanVideo 720p, 87 per CU) the one-item grid measured
-// 1% faster.
-constexpr int32_t PERSIST_MAX_ITEMS_PER_CU = 48;
+// Up to this many band items (256 query rows each) per CU the persistent grid below is used:
+// with few items per CU the per-XCD queue evens out the tail (Wan 480p, 20 items per CU: 3-6%
+// faster; CogVideoX, 13 per CU: 1-5%), while with more (HunyuanVideo 720p, 44 per CU) the
+// one-item grid measured 1% faster.
+constexpr int32_t PERSIST_MAX_ITEMS_PER_CU = 32;
 
 // The same work with one workgroup per CU that takes items until none are left.  Workgroup w
 // runs on XCD w % 8 (workgroups reach the XCDs round-robin) and takes the items the one-item

@@ -5,9 +5,11 @@
 // mask; each head keeps the mask whose output has the smaller mean squared error against
 // the unmasked output.
 //
-// Pass 1 (split-K): a workgroup of four wavefronts takes one (head, key range, group of 64
+// Pass 1 (split-K): a workgroup of four wavefronts takes one (head, key split, group of 64
 // sampled queries), 16 queries per wavefront, and two workgroups share a CU, so that one's
-// matrix products overlap the other's exponentials.  Per 64-key tile and wavefront, with
+// matrix products overlap the other's exponentials.  Split s of n holds the head's key tiles
+// s, s + n, s + 2n, ...: the n workgroups of a head, which run at the same time, stream
+// neighbouring tiles (3% faster at 720p than contiguous key ranges per split).  Per 64-key tile and wavefront, with
 // v_mfma_f32_16x16x32_bf16 (lane l: row/column l%16, k-quarter l/16):
 //   S^T[key][query] = K Q^T       A = K rows from LDS, B = the wavefront's Q rows, kept in
 //                                 registers; lane l holds 16 scores of query l%16.
@@ -50,11 +52,16 @@ constexpr int NKB = TILE / 16;     // 16-key score blocks per tile
 constexpr int NST = TILE / 32;     // 32-key PV steps per tile
 constexpr int QG = 64;             // sampled queries per workgroup
 constexpr int MAX_SPLIT = 128;
+constexpr int MERGE_PF = 32;       // splits whose partial outputs the merge loads up front
 constexpr int TARGET_WGS = 512;    // two workgroups per CU
 constexpr float RESCALE_SLACK = 8.0f;
 // A masked state's row sum in a split below this (relative to the split's unmasked reference)
 // may have lost keys to underflow; such a state is recomputed exactly.
 constexpr float UNDERFLOW_GUARD = 0x1p-100f;
+// Cache policy of the tile copies: non-temporal (nt), since every K and V row is read once.
+// Measured at 720p: the profiling call 0.327 -> 0.309 ms inside the layer and 0.350 -> 0.281 ms
+// with the caches flushed; the Wan-like grid 0.192 -> 0.160 ms.
+constexpr int CPOL_NT = 2;
 
 // s_waitcnt immediate (gfx9 encoding): at most vm vector-memory loads and lgkm LDS operations
 // outstanding, exports not waited for.
@@ -109,7 +116,7 @@ __device__ __forceinline__ void tile_copy(const bf16* __restrict__ src, int32_t 
     const int lc = pc ^ (is_v ? T::swz_v(row) : T::swz_k(row));
     const uint32_t boff = (uint32_t)min(k0 + row, S - 1) * (uint32_t)T::ROW_BYTES + 16u * (uint32_t)lc;
     __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(src) + boff,
-                                     (__attribute__((address_space(3))) void*)((char*)dst + blk * 1024), 16, 0, 0);
+                                     (__attribute__((address_space(3))) void*)((char*)dst + blk * 1024), 16, 0, CPOL_NT);
   }
 }
 
@@ -293,9 +300,12 @@ __global__ __launch_bounds__(NT, 2) void profile_partial_kernel(ProfileArgs a) {
   const bf16* __restrict__ K = a.k + off;
   const bf16* __restrict__ V = a.v + off;
 
-  const int32_t ks = split * a.keys_per_split;
-  const int32_t ke = min(a.S, ks + a.keys_per_split);
-  const int32_t ntiles = (ke - ks + TILE - 1) / TILE;
+  // this split's tiles: split, split + nsplit, split + 2 nsplit, ... of the head's key tiles
+  const int32_t n_tiles_all = (a.S + TILE - 1) / TILE;
+  const int32_t ntiles = split < n_tiles_all ? (n_tiles_all - 1 - split) / a.nsplit + 1 : 0;
+  const int32_t ks = split * TILE;
+  const int32_t kstride = a.nsplit * TILE;
+  const int32_t ke = a.S;
 
   // this lane's query: q = l%16 of the wavefront's 16
   const int32_t qi = zq * QG + wave * 16 + i16;
@@ -330,9 +340,9 @@ __global__ __launch_bounds__(NT, 2) void profile_partial_kernel(ProfileArgs a) {
   auto step = [&](int32_t t, const bf16* kt, const bf16* vt, bf16* kn, bf16* vn) {
     __builtin_amdgcn_s_waitcnt(waitcnt_imm((NBUF - 2) * T::CPW, 0));
     tile_barrier();
-    tile_copy<D>(K, ks + (t + NBUF - 1) * TILE, a.S, kn, wave, lane, false);
-    tile_copy<D>(V, ks + (t + NBUF - 1) * TILE, a.S, vn, wave, lane, true);
-    profile_tile<D, TPM>(st, qf, reinterpret_cast<const char*>(kt), vt, ks + t * TILE, ke, c, sp_lo,
+    tile_copy<D>(K, ks + (t + NBUF - 1) * kstride, a.S, kn, wave, lane, false);
+    tile_copy<D>(V, ks + (t + NBUF - 1) * kstride, a.S, vn, wave, lane, true);
+    profile_tile<D, TPM>(st, qf, reinterpret_cast<const char*>(kt), vt, ks + t * kstride, ke, c, sp_lo,
                          (uint32_t)(sp_hi - sp_lo), pq, a, lane);
   };
   for (int32_t t = 0; t < ntiles; t += NBUF) {
@@ -345,13 +355,19 @@ __global__ __launch_bounds__(NT, 2) void profile_partial_kernel(ProfileArgs a) {
   // ---- does this split hold keys of each mask for this lane's query? ----
   bool has_keys[3];
   has_keys[0] = true;
-  has_keys[1] = max(sp_lo, ks) < min(sp_hi, ke);
   {
+    // does the split hold a tile of key range [lo, hi] (hi >= lo)?  Its first tile >= the
+    // range's first is that tile plus the distance to the split's residue.
+    const int32_t ns = a.nsplit;
+    auto holds = [&](int32_t lo, int32_t hi) {
+      const int32_t t0 = lo / TILE, t1 = hi / TILE;
+      const int32_t t = t0 + ((split - t0) % ns + ns) % ns;
+      return t <= t1;
+    };
+    has_keys[1] = holds(sp_lo, sp_hi - 1);
     const int32_t plo = max(0, pq - a.w_p), phi = min(a.P - 1, pq + a.w_p);
-    const int32_t f0 = (int32_t)fdiv((uint32_t)ks, a.divP), f1 = (int32_t)fdiv((uint32_t)(ke - 1), a.divP);
-    bool any = f1 - f0 >= 2;
-    any = any || (f0 * a.P + phi >= ks && f0 * a.P + plo <= ke - 1);
-    any = any || (f1 > f0 && f1 * a.P + plo <= ke - 1);
+    bool any = false;
+    for (int32_t f = 0; f < a.F && !any; ++f) any = holds(f * a.P + plo, f * a.P + phi);
     has_keys[2] = any;
   }
 
@@ -463,12 +479,20 @@ __global__ __launch_bounds__(D) void profile_merge_kernel(ProfileArgs a) {
   const int tid = threadIdx.x;
   const int32_t nparts = a.nsplit;
   const int32_t qpad = a.n_zq * QG;
+  auto slot_of = [&](int x, int32_t p) { return (((size_t)bh * nparts + p) * 3 + x) * qpad + qg; };
   for (int t = tid; t < 3 * nparts; t += D) {
     const int x = t / nparts, p = t - (t / nparts) * nparts;
-    const size_t slot = (((size_t)bh * nparts + p) * 3 + x) * qpad + qg;
+    const size_t slot = slot_of(x, p);
     sm[x][p] = a.part_ml[slot * 2];
     sl[x][p] = a.part_ml[slot * 2 + 1];
   }
+  // the first MERGE_PF splits' partial outputs are fetched now, so that their latency overlaps
+  // that of the (m, l) loads and the weights
+  float pre[3][MERGE_PF];
+#pragma unroll
+  for (int x = 0; x < 3; ++x)
+#pragma unroll
+    for (int p = 0; p < MERGE_PF; ++p) pre[x][p] = p < nparts ? a.part_o[slot_of(x, p) * D + tid] : 0.f;
   __syncthreads();
   if (tid < 3) {
     // split p holds 2^(sm + log2 sl) of the state's mass; weights are taken against the largest
@@ -498,10 +522,10 @@ __global__ __launch_bounds__(D) void profile_merge_kernel(ProfileArgs a) {
       continue;
     }
     float s = 0.f;
-    for (int32_t p = 0; p < nparts; ++p) {
-      const size_t slot = (((size_t)bh * nparts + p) * 3 + x) * qpad + qg;
-      s = fmaf(wt[x][p], a.part_o[slot * D + tid], s);
-    }
+#pragma unroll
+    for (int p = 0; p < MERGE_PF; ++p)
+      if (p < nparts) s = fmaf(wt[x][p], pre[x][p], s);
+    for (int32_t p = MERGE_PF; p < nparts; ++p) s = fmaf(wt[x][p], a.part_o[slot_of(x, p) * D + tid], s);
     o3[x] = s;
   }
   const double dsp = (double)o3[1] - (double)o3[0];
@@ -562,9 +586,7 @@ ProfilePlan profile_plan(int32_t BH, int32_t S, int32_t D, int32_t n_q) {
   if (want > MAX_SPLIT) want = MAX_SPLIT;
   if (want > max_tiles) want = max_tiles;
   if (want < 1) want = 1;
-  const int64_t per = (S + want - 1) / want;
-  p.keys_per_split = (int32_t)(((per + TILE - 1) / TILE) * TILE);
-  p.nsplit = (int32_t)((S + p.keys_per_split - 1) / p.keys_per_split);
+  p.nsplit = (int32_t)want;
   const size_t slots = (size_t)BH * p.nsplit * 3 * (size_t)(p.n_zq * QG);
   p.ml_floats = slots * 2;
   p.o_floats = slots * (size_t)D;

@@ -63,7 +63,7 @@ __global__ __launch_bounds__(ROPE_THREADS) void qknorm_rope_kernel(RopeArgs a) {
 #pragma unroll
     for (int u = 0; u < ROPE_UNROLL; ++u) {
       const int64_t row = min(base + u * stride, total - 1);
-      raw[u] = in[row * LPR + lane_c];
+      raw[u] = __builtin_nontemporal_load(&in[row * LPR + lane_c]);
     }
   };
   const int64_t step = stride * ROPE_UNROLL;
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(ROPE_THREADS) void qknorm_rope_kernel(RopeArgs a) {
         o[2 * i] = (bf16)(aa * cs.x - bb * cs.y);
         o[2 * i + 1] = (bf16)(aa * cs.y + bb * cs.x);
       }
-      out[row * LPR + lane_c] = __builtin_bit_cast(u32x4, o);
+      __builtin_nontemporal_store(__builtin_bit_cast(u32x4, o), &out[row * LPR + lane_c]);
     }
   };
 

@@ -138,7 +138,7 @@ struct ProfileArgs {
   int32_t BH, S, F, P, D, w_f, w_p;
   FastDiv divP;
   float scale;
-  int32_t nsplit, keys_per_split;
+  int32_t nsplit;             // key splits: split s holds key tiles s, s + nsplit, ...
   float* part_ml;             // [BH][nsplit][3][n_zq*64][2]
   float* part_o;              // [BH][nsplit][3][n_zq*64][D]
   double* row_sq;             // [BH][n_q][2] squared errors of each sampled row
@@ -149,7 +149,7 @@ hipError_t launch_profile(const ProfileArgs& a, hipStream_t st);
 
 // Split-K plan of the profiling kernel, shared by the launcher and the workspace query.
 struct ProfilePlan {
-  int32_t n_zq, nsplit, keys_per_split;
+  int32_t n_zq, nsplit;
   size_t ml_floats, o_floats, sq_doubles;
 };
 ProfilePlan profile_plan(int32_t BH, int32_t S, int32_t D, int32_t n_q);
