@@ -9,8 +9,8 @@
 // sampled queries), 16 queries per wavefront, and two workgroups share a CU, so that one's
 // matrix products overlap the other's exponentials.  Split s of n holds the head's key tiles
 // s, s + n, s + 2n, ...: the n workgroups of a head, which run at the same time, stream
-// neighbouring tiles (3% faster at 720p than contiguous key ranges per split).  Per 64-key tile and wavefront, with
-// v_mfma_f32_16x16x32_bf16 (lane l: row/column l%16, k-quarter l/16):
+// neighbouring tiles (3% faster at 720p than contiguous key ranges per split).  Per 64-key
+// tile and wavefront, with v_mfma_f32_16x16x32_bf16 (lane l: row/column l%16, k-quarter l/16):
 //   S^T[key][query] = K Q^T       A = K rows from LDS, B = the wavefront's Q rows, kept in
 //                                 registers; lane l holds 16 scores of query l%16.
 //   O_x^T[d][query] += V^T P_x^T  for the three softmax states x (dense, spatial, temporal):
@@ -180,7 +180,7 @@ __device__ __forceinline__ void profile_tile(PState<D>& st, const bf16x8 (&qf)[D
       sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, qf[ks], sacc[kb], 0, 0, 0);
     }
 
-  // ---- keys past the split's end (last tile only) do not exist ----
+  // ---- keys past the sequence end (the head's last tile only) do not exist ----
   const int32_t kl = k0 + 4 * g;                // key of element (kb, r): kl + 16 kb + r
   if (k0 + TILE > ke) {
 #pragma unroll
