@@ -163,14 +163,14 @@ def host_cores():
 
 
 def cpu_baseline(q, k, v, kinds, g, w_f, w_p):
-    """The fp64 oracle on a bounded sample of the same layer: 6144 query rows of one spatial
+    """The fp64 oracle on a bounded sample of the same layer: 8192 query rows of one spatial
     and one temporal head against all S keys; token-level FLOPs / wall time."""
     import numpy as np
     import oracle.svg_oracle as O
     hc = host_cores()
     heads = [int(np.argmax(kinds == 0)), int(np.argmax(kinds == 1))]
     rng = np.random.default_rng(123)
-    rows = np.sort(rng.choice(g.S, 6144, replace=False))
+    rows = np.sort(rng.choice(g.S, 8192, replace=False))
     sc = 1.0 / math.sqrt(g.D)
     flops = 0.0
     elapsed = 0.0
@@ -184,7 +184,7 @@ def cpu_baseline(q, k, v, kinds, g, w_f, w_p):
         m = O.mask_rows(kind, rows, g.S, g.P, w_f, w_p)
         flops += 4.0 * g.D * float(m.sum())
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", **hc, "kind": "oracle",
-            "sample": "fp64 numpy oracle, sparse attention of 6144 sampled query rows of one spatial and one "
+            "sample": "fp64 numpy oracle, sparse attention of 8192 sampled query rows of one spatial and one "
                       f"temporal head of the layer (S={g.S}, D={g.D}) against all keys; token-level FLOPs",
             "seconds": round(elapsed, 2)}
 
