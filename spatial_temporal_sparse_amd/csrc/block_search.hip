@@ -40,24 +40,26 @@ __device__ __forceinline__ float wave_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 constexpr int BM_KT = BLOCK_K_ROWS;        // keys per tile = one key block
+constexpr int BM_TPI = 2;                  // key tiles per workgroup barrier
 
 // 8 wavefronts of 32 rows each hold the query block as MFMA B operands; key tiles of 64 rows are
-// the A operand from LDS (double-buffered in registers -> LDS, chunks XOR-swizzled by row).  The
-// accumulator S^T[key][query] gives lane l query l%32 and 16 keys per 32-key half; each lane
-// sums its 32 weights, the wavefront reduces over its lanes (DPP inside rows of 16 lanes, then
-// lane swaps across rows and halves: no LDS round trips, 2.3% faster than a shuffle tree at
-// 720p), and one thread adds the eight wavefronts' sums in a fixed order, one tile behind.  At most 128 VGPRs, so that two
-// workgroups (four wavefronts per SIMD) share a CU: one's exponentials run under the other's
-// matrix products (16% faster at D = 128 than one workgroup per CU at 130 VGPRs).
+// the A operand from LDS, chunks XOR-swizzled by row.  The tiles are copied HBM -> LDS by
+// buffer loads that write LDS directly (no register staging), two tiles per workgroup barrier,
+// the next two in flight while the current ones are used (3% faster at 720p than staging
+// through registers).  The accumulator S^T[key][query] gives lane l query l%32 and 16 keys
+// per 32-key half; each lane sums its 32 weights, the wavefront reduces over its lanes (DPP
+// inside rows of 16 lanes, then lane swaps across rows and halves: no LDS round trips, 2.3%
+// faster than a shuffle tree at 720p), and one thread adds the eight wavefronts' sums in a
+// fixed order, one iteration behind.  At most 128 VGPRs, so that two workgroups (four
+// wavefronts per SIMD) share a CU: one's exponentials run under the other's matrix products
+// (16% faster at D = 128 than one workgroup per CU at 130 VGPRs).
 template <int D>
 __global__ __launch_bounds__(BM_NT, 4) void block_mass_kernel(BlockMassArgs a) {
   constexpr int NKS = D / 16;
   constexpr int CPR = D / 8;
   constexpr int RPB = 16 / CPR;
-  constexpr int PER_T = BM_KT * CPR / BM_NT;      // 16-byte chunks per thread per tile
-  static_assert(PER_T >= 1, "tile too small for the workgroup");
-  __shared__ __attribute__((aligned(16))) bf16 kt[2][BM_KT * D];
-  __shared__ float part[2][BM_NT / 64];
+  __shared__ __attribute__((aligned(1024))) bf16 kt[2][BM_TPI][BM_KT * D];
+  __shared__ float part[2][BM_TPI][BM_NT / 64];
 
   const int32_t bh = blockIdx.x / a.nqb;
   const int32_t qb = blockIdx.x - bh * a.nqb;
@@ -76,37 +78,8 @@ __global__ __launch_bounds__(BM_NT, 4) void block_mass_kernel(BlockMassArgs a) {
   const float l2 = row < S ? a.lse[(size_t)bh * S + row] * 1.44269504088896340736f : INFINITY;
   float* out = a.mass + (size_t)blockIdx.x * a.nkb;
 
-  u32x4 pre[PER_T];
-  auto fetch = [&](int32_t t) {
-#pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      const int o = tid + BM_NT * i;
-      const int32_t kr = min(t * BM_KT + o / CPR, S - 1);
-      pre[i] = *reinterpret_cast<const u32x4*>(kh + (size_t)kr * D + 8 * (o % CPR));
-    }
-  };
-  auto stash = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      const int o = tid + BM_NT * i;
-      const int r = o / CPR, q = o % CPR;
-      *reinterpret_cast<u32x4*>(&kt[buf][r * D + 8 * (q ^ ((r / RPB) & (CPR - 1)))]) = pre[i];
-    }
-  };
-  const int32_t nt = a.nkb;
-  fetch(0);
-  stash(0);
-  __syncthreads();
-  for (int32_t t = 0; t < nt; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < nt) fetch(t + 1);
-    if (tid == 0 && t > 0) {
-      const float* pp = part[buf ^ 1];
-      float s = 0.f;
-#pragma unroll
-      for (int w = 0; w < BM_NT / 64; ++w) s += pp[w];
-      out[t - 1] = s;
-    }
+  // one key tile's masses for this wavefront's 32 rows (the tile in LDS at ktile)
+  auto tile_mass = [&](const bf16* ktile, int32_t t) -> float {
     f32x16 acc[2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
@@ -121,7 +94,7 @@ __global__ __launch_bounds__(BM_NT, 4) void block_mass_kernel(BlockMassArgs a) {
       for (int blk = 0; blk < 2; ++blk) {
         const int r = blk * 32 + l32;
         const bf16x8 ka =
-            *reinterpret_cast<const bf16x8*>(&kt[buf][r * D + 8 * ((2 * s + hh) ^ ((r / RPB) & (CPR - 1)))]);
+            *reinterpret_cast<const bf16x8*>(&ktile[r * D + 8 * ((2 * s + hh) ^ ((r / RPB) & (CPR - 1)))]);
         acc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], acc[blk], 0, 0, 0);
       }
     __builtin_amdgcn_s_setprio(0);
@@ -157,20 +130,66 @@ __global__ __launch_bounds__(BM_NT, 4) void block_mass_kernel(BlockMassArgs a) {
           }
       }
       // a skipped tile's wavefront sum is exactly 0 and needs no reduction
-      s = sum0 + sum1;
-      s = wave_sum(s);
+      s = wave_sum(sum0 + sum1);
     }
-    if (lane == 0) part[buf][wave] = s;
-    if (t + 1 < nt) stash(buf ^ 1);
+    return s;
+  };
+  // Rows past the sequence end lie outside the buffer, read as zero and are masked by kend.
+  constexpr int ROW_BYTES = D * 2;
+  constexpr int RPI = 1024 / ROW_BYTES;                       // tile rows per 1 KB instruction
+  constexpr int IPW = BM_KT * ROW_BYTES / 1024 / (BM_NT / 64);  // instructions per wavefront and tile
+  static_assert(IPW >= 1, "tile too small for the workgroup");
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc((void*)kh, (short)0, (int)(uint32_t)((uint32_t)S * ROW_BYTES), 0x00020000);
+  auto dma = [&](int32_t t, bf16* dst) {
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int blkno = wave * IPW + i;
+      const int r = blkno * RPI + lane / CPR;
+      const int ch = (lane % CPR) ^ ((r / RPB) & (CPR - 1));
+      const uint32_t voff = (uint32_t)(t * BM_KT + r) * ROW_BYTES + 16u * (uint32_t)ch;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)((char*)dst + blkno * 1024),
+                                               16, voff, 0, 0, 0);
+    }
+  };
+  const int32_t nt = a.nkb;
+  const int32_t ni = (nt + BM_TPI - 1) / BM_TPI;
+  auto issue = [&](int32_t it, int stage) {
+#pragma unroll
+    for (int u = 0; u < BM_TPI; ++u)
+      if (it * BM_TPI + u < nt) dma(it * BM_TPI + u, kt[stage][u]);
+  };
+  auto flush = [&](int32_t it, int stage) {     // thread 0: the block masses of iteration it
+#pragma unroll
+    for (int u = 0; u < BM_TPI; ++u) {
+      const int32_t t = it * BM_TPI + u;
+      if (t < nt) {
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < BM_NT / 64; ++w) s += part[stage][u][w];
+        out[t] = s;
+      }
+    }
+  };
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(VMCNT0);
+  __syncthreads();
+  for (int32_t it = 0; it < ni; ++it) {
+    const int stage = it & 1;
+    if (it + 1 < ni) issue(it + 1, stage ^ 1);
+    if (tid == 0 && it > 0) flush(it - 1, stage ^ 1);
+#pragma unroll
+    for (int u = 0; u < BM_TPI; ++u) {
+      const int32_t t = it * BM_TPI + u;
+      if (t < nt) {
+        const float s = tile_mass(kt[stage][u], t);
+        if (lane == 0) part[stage][u][wave] = s;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(VMCNT0);
     __syncthreads();
   }
-  if (tid == 0) {
-    const float* pp = part[(nt - 1) & 1];
-    float s = 0.f;
-#pragma unroll
-    for (int w = 0; w < BM_NT / 64; ++w) s += pp[w];
-    out[nt - 1] = s;
-  }
+  if (tid == 0) flush(ni - 1, (ni - 1) & 1);
 }
 
 // Per (head, query block): bitonic sort of (mass, block) in LDS, decreasing mass and increasing
