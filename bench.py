@@ -12,9 +12,10 @@ seeded inputs (B=1, H=24, F=33 x 45 x 80 tokens = 118800, D=128, bf16, half the 
 planted spatial and half temporal; w_f = 1 frame, w_p = 64 positions).
 
 Prints one JSON line on stdout (progress goes to stderr).  `value` is the effective
-attention throughput of the whole step: FLOPs of the computed attention tiles (4*D per
-query-key pair of every 128x64 tile the schedule computes, clipped at the sequence end)
-divided by the step time.
+attention throughput of the whole step: FLOPs of the attention tiles (4*D per query-key pair
+of every 128x64 tile of the exported block mask, clipped at the sequence end) divided by the
+step time.  The kernel's 256-row workgroups walk the union of two 128-row blocks' key runs,
+about 2% more work at 720p, which this count leaves out.
 """
 import argparse
 import hashlib
@@ -84,7 +85,9 @@ def copy_calibration():
 
 
 def tile_flops(svg, kind, g, w_f, w_p, bm, bn):
-    """FLOPs of the tiles the schedule computes (from the library's exported block mask)."""
+    """FLOPs of the 128x64 tiles of the library's exported block mask: each 128-row query block's
+    run of key tiles.  The attention kernel's 256-row workgroups walk the union of two such runs,
+    slightly more work (about 2% at 720p), which this count leaves out."""
     import torch
     mask = svg.build_block_mask(kind, g.F, g.HH, g.WW, w_f, w_p, bm, bn).to(torch.float64)
     S = g.S
